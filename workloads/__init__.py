@@ -1,0 +1,195 @@
+"""Seeded synthetic inputs for the attention library and its oracle.
+
+This module holds no attention arithmetic: it draws random numbers, rounds
+them to the storage precision, builds masks' valid lengths and paged block
+tables, and describes the five workloads.  Both the GPU tests and the fp64
+oracle are fed from here, so both see bit-identical inputs.
+
+Storage precision: bf16 values are produced by round-to-nearest-even of fp32
+draws (any multiplier such as x0.5 is applied in fp32 before rounding) and are
+returned as raw uint16 bits plus their exact float64 value.
+
+Seeds: ``numpy.random.default_rng([cfg, tensor_id])`` (PCG64) with tensor ids
+Q=0, K=1, V=2, dO=3, lengths=4, block permutation=5, K cache=6, V cache=7.
+"""
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+TID_Q, TID_K, TID_V, TID_DO, TID_LEN, TID_PERM, TID_KC, TID_VC = range(8)
+
+
+def rng(cfg_seed, tensor_id):
+    return np.random.default_rng([int(cfg_seed), int(tensor_id)])
+
+
+def bf16_bits(x):
+    """fp32 array -> uint16 bf16 bits, round to nearest even (NaN kept NaN)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r = np.where(nan, np.uint16(0x7FC0), r)
+    return r
+
+
+def bf16_value(bits):
+    """uint16 bf16 bits -> float32 array holding the same value exactly."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class Tensor:
+    """A generated tensor: storage bits (bf16) or fp32 data, plus exact fp64."""
+    dtype: str            # "bf16" or "f32"
+    store: np.ndarray     # uint16 bits for bf16, float32 for f32
+    exact: np.ndarray     # float64 copy of the stored values
+
+    @property
+    def shape(self):
+        return self.store.shape
+
+
+def normal(shape, cfg_seed, tensor_id, dtype, mult=1.0):
+    """iid N(0,1) * mult, drawn in fp32, stored in ``dtype``."""
+    x = rng(cfg_seed, tensor_id).standard_normal(size=shape, dtype=np.float32)
+    if mult != 1.0:
+        x = (x * np.float32(mult)).astype(np.float32)
+    if dtype == "bf16":
+        bits = bf16_bits(x)
+        return Tensor("bf16", bits, bf16_value(bits).astype(np.float64))
+    if dtype == "f32":
+        return Tensor("f32", x, x.astype(np.float64))
+    raise ValueError(dtype)
+
+
+def uniform_int(n, lo, hi, cfg_seed, tensor_id):
+    """n integers uniform on [lo, hi] inclusive (int32)."""
+    return rng(cfg_seed, tensor_id).integers(lo, hi + 1, size=n).astype(np.int32)
+
+
+@dataclass
+class Paged:
+    """A paged KV cache: [num_blocks, block_size, Hkv, d] plus block table."""
+    k_cache: Tensor
+    v_cache: Tensor
+    block_table: np.ndarray   # int32 [B, max_blocks], -1 where unused
+    seq_lens: np.ndarray      # int32 [B]
+    block_size: int
+
+
+def paged_cache(seq_lens, Hkv, d, block_size, max_blocks, cfg_seed,
+                poison_tails=True):
+    """Random paged cache: every sequence's blocks are a slice of one random
+    permutation of all physical blocks; slots past a sequence's length in its
+    last block hold NaN when ``poison_tails`` (so a kernel that reads them
+    into its arithmetic is caught), else ordinary N(0,1) values."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = seq_lens.size
+    nblk = [-(-int(L) // block_size) for L in seq_lens]
+    total = max(1, sum(nblk))
+    perm = rng(cfg_seed, TID_PERM).permutation(total).astype(np.int32)
+    table = np.full((B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :nblk[b]] = perm[off:off + nblk[b]]
+        off += nblk[b]
+    shape = (total, block_size, Hkv, d)
+    kc = rng(cfg_seed, TID_KC).standard_normal(size=shape, dtype=np.float32)
+    vc = rng(cfg_seed, TID_VC).standard_normal(size=shape, dtype=np.float32)
+    if poison_tails:
+        for b in range(B):
+            L = int(seq_lens[b])
+            if nblk[b] and L % block_size:
+                last = table[b, nblk[b] - 1]
+                kc[last, L % block_size:] = np.nan
+                vc[last, L % block_size:] = np.nan
+    kb, vb = bf16_bits(kc), bf16_bits(vc)
+    return Paged(Tensor("bf16", kb, bf16_value(kb).astype(np.float64)),
+                 Tensor("bf16", vb, bf16_value(vb).astype(np.float64)),
+                 table, seq_lens, block_size)
+
+
+@dataclass
+class Workload:
+    """One attention workload (a forward/backward problem or a decode batch)."""
+    name: str
+    seed: int
+    kind: str                 # "attn" or "decode"
+    dtype: str                # "bf16" or "f32"
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool = False
+    qkv_mult: float = 1.0
+    kv_len_range: Optional[tuple] = None   # (lo, hi) inclusive, key padding
+    backward: bool = False
+    # decode only
+    Hkv: int = 0
+    ctx_range: Optional[tuple] = None
+    block_size: int = 16
+    splits: int = 8
+    notes: str = field(default="")
+
+    def qkv(self):
+        shape = (self.B, self.H, self.N, self.d)
+        return tuple(normal(shape, self.seed, t, self.dtype, self.qkv_mult)
+                     for t in (TID_Q, TID_K, TID_V))
+
+    def dout(self):
+        return normal((self.B, self.H, self.N, self.d), self.seed, TID_DO,
+                      self.dtype)
+
+    def kv_len(self):
+        if self.kv_len_range is None:
+            return None
+        lo, hi = self.kv_len_range
+        return uniform_int(self.B, lo, hi, self.seed, TID_LEN)
+
+    def decode_inputs(self, poison_tails=True):
+        lens = uniform_int(self.B, self.ctx_range[0], self.ctx_range[1],
+                           self.seed, TID_LEN)
+        max_blocks = -(-self.ctx_range[1] // self.block_size)
+        cache = paged_cache(lens, self.Hkv, self.d, self.block_size,
+                            max_blocks, self.seed, poison_tails)
+        q = normal((self.B, self.H, self.d), self.seed, TID_Q, self.dtype)
+        return q, cache
+
+    def fwd_flops(self):
+        """4*B*H*N^2*d, halved when causal (nominal N^2 under key padding)."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def bwd_flops(self):
+        """Five N^2 d contractions: 2.5x the forward count."""
+        return 2.5 * self.fwd_flops()
+
+
+# The five workloads.  Shapes follow BERT-large / GPT-2-medium / long-context
+# attention layers; the data are synthetic (no datasets or trained weights).
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", 1, "attn", "f32", 1, 1, 256, 64),
+    "bert_large_padded": Workload(
+        "bert_large_padded", 2, "attn", "bf16", 16, 16, 512, 64,
+        kv_len_range=(256, 512), backward=True),
+    "gpt2_medium_causal_1k": Workload(
+        "gpt2_medium_causal_1k", 3, "attn", "bf16", 8, 16, 1024, 64,
+        causal=True, qkv_mult=0.5, backward=True),
+    "gpt2_medium_causal_4k": Workload(
+        "gpt2_medium_causal_4k", 31, "attn", "bf16", 2, 16, 4096, 64,
+        causal=True, qkv_mult=0.5, backward=True),
+    "long_causal_16k_d128": Workload(
+        "long_causal_16k_d128", 4, "attn", "bf16", 1, 16, 16384, 128,
+        causal=True),
+    "long_causal_64k_d64": Workload(
+        "long_causal_64k_d64", 41, "attn", "bf16", 1, 2, 65536, 64,
+        causal=True),
+    "paged_gqa_decode": Workload(
+        "paged_gqa_decode", 5, "decode", "bf16", 16, 32, 1, 128, Hkv=8,
+        ctx_range=(1024, 8192), block_size=16, splits=8),
+}
