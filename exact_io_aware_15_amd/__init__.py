@@ -1,0 +1,159 @@
+"""fa355: exact, IO-aware attention on AMD MI355X (gfx950).
+
+A thin binding over libfa355's C ABI (include/fa355.h).  It checks tensor
+dtypes, shapes and devices, allocates outputs and workspaces with PyTorch, and
+passes raw device pointers plus the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no fallback path: if
+the library is missing, the calls raise.
+
+    o, m, l = fwd(q, k, v, causal=False, kv_len=None, scale=None)
+    dq, dk, dv = bwd(q, k, v, o, do, m, l, causal=False, kv_len=None)
+    out = decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits=8)
+"""
+
+import math
+
+from ._lib import FA_BF16, FA_F32, FaError, LibraryMissing, check, lib
+
+__all__ = ["fwd", "bwd", "decode_paged", "bwd_workspace_bytes",
+           "decode_workspace_bytes", "FaError", "LibraryMissing"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check_dev(name, t, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, "
+                         f"got {tuple(t.shape)}")
+
+
+def _stream(t):
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _kv_len(kv_len, B, device):
+    torch = _torch()
+    if kv_len is None:
+        return None
+    if not torch.is_tensor(kv_len):
+        kv_len = torch.tensor(list(kv_len), dtype=torch.int32, device=device)
+    _check_dev("kv_len", kv_len, torch.int32, (B,))
+    return kv_len
+
+
+def fwd(q, k, v, causal=False, kv_len=None, scale=None, return_stats=True):
+    """Exact attention forward.  q, k, v: [B,H,N,d] bf16 or fp32 on the GPU.
+
+    Returns (o, m, l): o like q; m, l fp32 [B,H,N] (None if not requested).
+    """
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check_dev("q", q)
+    _check_dev("k", k, q.dtype, q.shape)
+    _check_dev("v", v, q.dtype, q.shape)
+    kv_len = _kv_len(kv_len, B, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    m = l = None
+    if return_stats:
+        m = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        l = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib().fa_fwd(_dtype_code(q), B, H, N, d, _ptr(q), _ptr(k),
+                          _ptr(v), _ptr(o), _ptr(m), _ptr(l), _ptr(kv_len),
+                          int(bool(causal)), scale, _stream(q))
+    check("fa_fwd", st)
+    return o, m, l
+
+
+def bwd_workspace_bytes(B, H, N, d):
+    return int(lib().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def bwd(q, k, v, o, do, m, l, causal=False, kv_len=None, scale=None,
+        workspace=None):
+    """Gradients (dq, dk, dv) of exact attention; all bf16 [B,H,N,d]."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_dev(name, t, torch.bfloat16, (B, H, N, d))
+    _check_dev("m", m, torch.float32, (B, H, N))
+    _check_dev("l", l, torch.float32, (B, H, N))
+    kv_len = _kv_len(kv_len, B, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    with torch.cuda.device(q.device):
+        st = lib().fa_bwd(B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                          _ptr(do), _ptr(m), _ptr(l), _ptr(kv_len),
+                          int(bool(causal)), scale, _ptr(dq), _ptr(dk),
+                          _ptr(dv), _ptr(workspace), workspace.numel(),
+                          _stream(q))
+    check("fa_bwd", st)
+    return dq, dk, dv
+
+
+def decode_workspace_bytes(B, Hq, d, num_splits):
+    return int(lib().fa_decode_workspace_bytes(B, Hq, d, num_splits))
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits=8,
+                 scale=None, workspace=None):
+    """Single-token GQA decode over a paged cache.
+
+    q: [B,Hq,d] bf16; k_cache, v_cache: [num_blocks, block_size, Hkv, d] bf16;
+    block_table: int32 [B, max_blocks]; seq_lens: int32 [B].  Returns out
+    [B,Hq,d] bf16.
+    """
+    torch = _torch()
+    B, Hq, d = q.shape
+    nb, bs, Hkv, dk = k_cache.shape
+    _check_dev("q", q, torch.bfloat16)
+    _check_dev("k_cache", k_cache, torch.bfloat16)
+    _check_dev("v_cache", v_cache, torch.bfloat16, k_cache.shape)
+    if dk != d:
+        raise ValueError("k_cache head dim differs from q")
+    _check_dev("block_table", block_table, torch.int32)
+    _check_dev("seq_lens", seq_lens, torch.int32, (B,))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = decode_workspace_bytes(B, Hq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8,
+                                device=q.device)
+    out = torch.empty_like(q)
+    with torch.cuda.device(q.device):
+        st = lib().fa_decode_paged(B, Hq, Hkv, d, _ptr(q), _ptr(k_cache),
+                                   _ptr(v_cache), nb, bs, _ptr(block_table),
+                                   block_table.shape[1], _ptr(seq_lens),
+                                   num_splits, scale, _ptr(out),
+                                   _ptr(workspace), workspace.numel(),
+                                   _stream(q))
+    check("fa_decode_paged", st)
+    return out

@@ -1,0 +1,64 @@
+"""ctypes loader for libfa355.so (the C ABI declared in include/fa355.h).
+
+The library is required: if it has not been built, every entry point raises
+instead of falling back to any other implementation.
+"""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "libfa355.so")
+
+FA_F32, FA_BF16 = 0, 1
+STATUS = {0: "FA_OK", -1: "FA_E_NULLPTR", -2: "FA_E_SHAPE",
+          -3: "FA_E_UNSUPPORTED", -4: "FA_E_WORKSPACE", -5: "FA_E_HIP"}
+
+# Every function the header declares, with its ctypes signature.
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "fa_status_str": (ctypes.c_char_p, [_I]),
+    "fa_fwd": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _F,
+                    _P]),
+    "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "fa_bwd": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F,
+                    _P, _P, _P, _P, _Z, _P]),
+    "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "fa_decode_paged": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P,
+                             _I, _F, _P, _P, _Z, _P]),
+}
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class FaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def lib():
+    """Load libfa355.so once and attach the declared signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryMissing(
+                f"{LIB_PATH} is not built: run "
+                "`python -m exact_io_aware_15_amd.build` (needs ROCm hipcc)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def check(fn, status):
+    if status != 0:
+        raise FaError(fn, status)

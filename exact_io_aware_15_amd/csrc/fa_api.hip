@@ -1,0 +1,148 @@
+// fa_api.hip -- the C ABI of libfa355 (declared in include/fa355.h):
+// argument validation, workspace sizing and dispatch to the gfx950 kernels.
+// Validation touches no device memory and calls no HIP function, so an invalid
+// call returns its status with no side effect (also on a machine with no GPU).
+#include <math.h>
+
+#include "fa355.h"
+#include "fa_kernels.h"
+
+using namespace fa355;
+
+namespace {
+
+constexpr int kMaxN = 1 << 20;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool valid_scale(float s) { return isfinite(s) && s > 0.f; }
+
+// Element counts must fit the kernels' int row indices and size_t offsets.
+bool attn_shape_ok(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1 || N > kMaxN) return false;
+  return (long long)B * H * N <= (1LL << 31) - 1;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_E_NULLPTR: return "FA_E_NULLPTR: a required pointer is NULL";
+    case FA_E_SHAPE: return "FA_E_SHAPE: size out of range or inconsistent";
+    case FA_E_UNSUPPORTED: return "FA_E_UNSUPPORTED: not implemented in this build";
+    case FA_E_WORKSPACE: return "FA_E_WORKSPACE: workspace missing or too small";
+    case FA_E_HIP: return "FA_E_HIP: HIP runtime error at launch";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_fwd(int dtype, int B, int H, int N, int d, const void *q,
+           const void *k, const void *v, void *o, float *m, float *l,
+           const int32_t *kv_len, int causal, float scale, void *stream) {
+  if (!q || !k || !v || !o) return FA_E_NULLPTR;
+  if ((m == nullptr) != (l == nullptr)) return FA_E_NULLPTR;
+  if (!attn_shape_ok(B, H, N) || !valid_scale(scale)) return FA_E_SHAPE;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_E_UNSUPPORTED;
+  FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.m = m; a.l = l; a.kv_len = kv_len;
+  a.B = B; a.H = H; a.N = N; a.BH = B * H;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == FA_BF16) return from_hip(launch_fwd_bf16(a, d, causal != 0, s));
+  return from_hip(launch_fwd_f32(a, d, causal != 0, s));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (!attn_shape_ok(B, H, N) || (d != 64 && d != 128)) return 0;
+  const size_t rows = (size_t)B * H * N;
+  return align_up(rows * d * sizeof(float)) + 2 * align_up(rows * sizeof(float));
+}
+
+int fa_bwd(int B, int H, int N, int d, const void *q, const void *k,
+           const void *v, const void *o, const void *dout, const float *m,
+           const float *l, const int32_t *kv_len, int causal, float scale,
+           void *dq, void *dk, void *dv, void *workspace,
+           size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !o || !dout || !m || !l || !dq || !dk || !dv)
+    return FA_E_NULLPTR;
+  if (!attn_shape_ok(B, H, N) || !valid_scale(scale)) return FA_E_SHAPE;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
+  if (((uintptr_t)workspace) % kAlign) return FA_E_WORKSPACE;
+  const size_t rows = (size_t)B * H * N;
+  BwdArgs a;
+  a.q = (const uint16_t *)q; a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v; a.o = (const uint16_t *)o;
+  a.dout = (const uint16_t *)dout; a.m = m; a.l = l; a.kv_len = kv_len;
+  a.dq = (uint16_t *)dq; a.dk = (uint16_t *)dk; a.dv = (uint16_t *)dv;
+  char *ws = (char *)workspace;
+  a.dq_acc = (float *)ws;
+  a.lse2 = (float *)(ws + align_up(rows * d * sizeof(float)));
+  a.delta = (float *)(ws + align_up(rows * d * sizeof(float)) +
+                      align_up(rows * sizeof(float)));
+  a.B = B; a.H = H; a.N = N; a.BH = B * H;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  return from_hip(launch_bwd(a, d, causal != 0, (hipStream_t)stream));
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
+  if (B < 1 || Hq < 1 || (d != 64 && d != 128) || num_splits < 1 ||
+      num_splits > 64)
+    return 0;
+  const size_t parts = (size_t)B * Hq * num_splits;
+  return 2 * align_up(parts * sizeof(float)) +
+         align_up(parts * d * sizeof(float));
+}
+
+int fa_decode_paged(int B, int Hq, int Hkv, int d, const void *q,
+                    const void *k_cache, const void *v_cache, int num_blocks,
+                    int block_size, const int32_t *block_table,
+                    int max_blocks_per_seq, const int32_t *seq_lens,
+                    int num_splits, float scale, void *out, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
+    return FA_E_NULLPTR;
+  if (B < 1 || Hq < 1 || Hkv < 1 || num_blocks < 1 ||
+      max_blocks_per_seq < 1 || num_splits < 1 || num_splits > 64 ||
+      !valid_scale(scale))
+    return FA_E_SHAPE;
+  if (Hq % Hkv != 0) return FA_E_SHAPE;
+  if (Hq / Hkv > 16) return FA_E_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  if (block_size != 16) return FA_E_UNSUPPORTED;
+  if ((long long)B * max_blocks_per_seq > (1LL << 31) - 1 ||
+      (long long)num_blocks * block_size * Hkv * d > (1LL << 40))
+    return FA_E_SHAPE;
+  const size_t need = fa_decode_workspace_bytes(B, Hq, d, num_splits);
+  if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
+  if (((uintptr_t)workspace) % kAlign) return FA_E_WORKSPACE;
+  const size_t parts = (size_t)B * Hq * num_splits;
+  DecodeArgs a;
+  a.q = (const uint16_t *)q;
+  a.k_cache = (const uint16_t *)k_cache;
+  a.v_cache = (const uint16_t *)v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = (uint16_t *)out;
+  char *ws = (char *)workspace;
+  a.part_m = (float *)ws;
+  a.part_l = (float *)(ws + align_up(parts * sizeof(float)));
+  a.part_o = (float *)(ws + 2 * align_up(parts * sizeof(float)));
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_blocks = max_blocks_per_seq;
+  a.num_splits = num_splits;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  return from_hip(launch_decode(a, d, (hipStream_t)stream));
+}
+
+}  // extern "C"

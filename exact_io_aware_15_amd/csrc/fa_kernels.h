@@ -1,0 +1,54 @@
+// fa_kernels.h -- argument blocks and launchers of the gfx950 kernels
+// (internal to libfa355; the public C ABI is include/fa355.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa355 {
+
+struct FwdArgs {
+  const void *q, *k, *v;   // [B,H,N,d] bf16 or fp32
+  void *o;                 // [B,H,N,d]
+  float *m, *l;            // [B,H,N] or both null
+  const int32_t *kv_len;   // [B] or null
+  int B, H, N, BH;
+  float scale;             // natural-units score scale
+  float c;                 // scale * log2(e): scores enter exp2 in log2 units
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool causal,
+                           hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal,
+                          hipStream_t s);
+
+struct BwdArgs {
+  const uint16_t *q, *k, *v, *o, *dout;  // [B,H,N,d] bf16
+  const float *m, *l;                    // [B,H,N]
+  const int32_t *kv_len;                 // [B] or null
+  uint16_t *dq, *dk, *dv;                // [B,H,N,d] bf16
+  float *dq_acc;                         // [B,H,N,d] fp32 workspace
+  float *lse2;                           // [B,H,N] workspace: log2-domain row offset
+  float *delta;                          // [B,H,N] workspace: rowsum(dO*O)
+  int B, H, N, BH;
+  float scale, c;
+};
+
+hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, hipStream_t s);
+
+struct DecodeArgs {
+  const uint16_t *q;            // [B,Hq,d]
+  const uint16_t *k_cache;      // [num_blocks, block_size, Hkv, d]
+  const uint16_t *v_cache;
+  const int32_t *block_table;   // [B, max_blocks]
+  const int32_t *seq_lens;      // [B]
+  uint16_t *out;                // [B,Hq,d]
+  float *part_m, *part_l;       // [B,Hq,S]
+  float *part_o;                // [B,Hq,S,d]
+  int B, Hq, Hkv, max_blocks, num_splits;
+  float scale, c;
+};
+
+hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t s);
+
+}  // namespace fa355

@@ -1,0 +1,163 @@
+/*
+ * fa355.h -- C ABI of libfa355: exact, IO-aware attention on AMD MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   "FA notes"  = the close-reading notes "精读笔记 08：FlashAttention"
+ *                 (llm-papers-study.pages.dev) on the FlashAttention paper;
+ *   "S12"       = chapter "S12 FlashAttention" of an LLM-inference course
+ *                 (llminference.xinbetween.com/zh/s12).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates, frees and caches nothing, and keeps no state between calls.
+ *   - Every call only enqueues work on `stream` (a hipStream_t passed as void*;
+ *     NULL means the null stream) and returns without synchronising.  Calls are
+ *     reentrant; calls that share output or workspace buffers must be ordered
+ *     by the caller.
+ *   - Arguments are validated before anything is launched.  An invalid argument
+ *     returns a negative fa_status and has no side effect.  A launch failure
+ *     reported by the HIP runtime returns FA_E_HIP.  The contents of device
+ *     arrays (kv_len values, block-table entries, sequence lengths) are the
+ *     caller's contract and are not checked.
+ *   - Tensors are contiguous, row-major, with the layouts stated per argument.
+ *     bf16 means IEEE bfloat16 storage; results are rounded to nearest even.
+ *   - The score scale is applied before the row max: S = scale * Q K^T.  S12's
+ *     recurrence uses scale = 1/sqrt(d); FA notes §2.1 states the unscaled form.
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_E_NULLPTR = -1,     /* a required pointer is NULL                         */
+  FA_E_SHAPE = -2,       /* a size is out of range or inconsistent             */
+  FA_E_UNSUPPORTED = -3, /* valid request this build does not implement        */
+  FA_E_WORKSPACE = -4,   /* workspace missing or smaller than the query says   */
+  FA_E_HIP = -5          /* the HIP runtime reported an error at launch        */
+} fa_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *fa_status_str(int status);
+
+/*
+ * fa_fwd -- exact attention forward, O = softmax(scale * Q K^T) V.
+ *
+ * Computes FA notes §2.1 (standard attention) with the tiled, fused method of
+ * FA notes §3.2 / §3.4: key/value tiles stream through on-chip memory and the
+ * online-softmax recurrence of FA notes §3.1 / S12 ("core idea") carries the
+ * running max m and sum l, so the N x N score matrix never reaches HBM.
+ *
+ *   dtype   FA_BF16 (bf16 in and out, fp32 accumulation) or FA_F32 (fp32).
+ *   B, H    batch and heads, >= 1.
+ *   N       sequence length, 1 <= N <= 1<<20 (queries and keys alike).
+ *   d       head dimension, 64 or 128.
+ *   q,k,v   [B,H,N,d] of `dtype`.
+ *   o       [B,H,N,d] of `dtype`, written.
+ *   m, l    [B,H,N] fp32, written, or both NULL to skip.  m is the row max of
+ *           the scaled visible scores (natural-log units) and l = sum over
+ *           visible keys of exp(S - m): the statistics FA notes §3.3 keeps for
+ *           the backward pass.  A row with no visible key gets o = 0, l = 0,
+ *           m = -inf.
+ *   kv_len  NULL (all N keys valid) or device int32 [B]: keys j >= kv_len[b]
+ *           are masked for batch b (key padding).  Values must be in [0, N].
+ *   causal  nonzero: key j is visible to query i only if j <= i.
+ *   scale   score scale, finite and > 0 (1/sqrt(d) for standard attention).
+ *   stream  hipStream_t.
+ * Masked scores are excluded exactly (never a finite penalty); the running
+ * max starts at a finite negative so a fully masked tile cannot produce NaN
+ * (S12, box on exp(-inf - -inf)).
+ */
+int fa_fwd(int dtype, int B, int H, int N, int d,
+           const void *q, const void *k, const void *v, void *o,
+           float *m, float *l, const int32_t *kv_len, int causal, float scale,
+           void *stream);
+
+/*
+ * fa_bwd_workspace_bytes -- device workspace fa_bwd needs for this shape:
+ * an fp32 dQ accumulator [B,H,N,d] plus two fp32 row vectors [B,H,N].
+ * Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * fa_bwd -- gradients of exact attention by recomputation (FA notes §3.3):
+ * score and probability tiles are rebuilt on chip from Q, K and the saved
+ * statistics (m, l) instead of being stored.  The gradient formulas are the
+ * softmax chain rule (the pages do not print them):
+ *   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ *   B, H, N, d, kv_len, causal, scale   as for fa_fwd (bf16 only).
+ *   q, k, v, o, dout  [B,H,N,d] bf16: the forward inputs, its output and dL/dO.
+ *   m, l              [B,H,N] fp32 as written by fa_fwd for the same inputs.
+ *   dq, dk, dv        [B,H,N,d] bf16, all written.  Keys masked by kv_len get
+ *                     dk = dv = 0 exactly.
+ *   workspace         device memory of at least fa_bwd_workspace_bytes(...)
+ *                     bytes, 256-byte aligned; contents on entry are ignored.
+ */
+int fa_bwd(int B, int H, int N, int d,
+           const void *q, const void *k, const void *v, const void *o,
+           const void *dout, const float *m, const float *l,
+           const int32_t *kv_len, int causal, float scale,
+           void *dq, void *dk, void *dv,
+           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * fa_decode_workspace_bytes -- device workspace fa_decode_paged needs: the
+ * per-split partial triples (m, l, o) in fp32.  Returns 0 for invalid sizes.
+ */
+size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
+
+/*
+ * fa_decode_paged -- one decode step: each sequence's single query token
+ * attends to its whole paged KV cache.
+ *
+ * S12 ("implement it") gives the paged loop: logical block t of sequence b
+ * lives in physical block block_table[b*max_blocks_per_seq + t] and the last
+ * block holds n = min(block_size, seq_len - t*block_size) valid slots.  S12's
+ * production-practice paragraph adds GQA head sharing and its "unlocks"
+ * paragraph gives flash-decoding: the key range is split over workers whose
+ * partial (m, l, o) triples are merged with the FA notes §3.1 rule.
+ *
+ *   B            sequences (>= 1).
+ *   Hq, Hkv      query and KV heads; Hq % Hkv == 0, query head h reads KV head
+ *                h / (Hq / Hkv); Hq / Hkv <= 16.
+ *   d            head dimension, 64 or 128.
+ *   q            [B,Hq,d] bf16.
+ *   k_cache,
+ *   v_cache      [num_blocks, block_size, Hkv, d] bf16.  Slots past a
+ *                sequence's length are never read into the arithmetic (they
+ *                may hold anything, NaN included).
+ *   block_size   tokens per block; 16.
+ *   block_table  device int32 [B, max_blocks_per_seq]; entries for t <
+ *                ceil(seq_len/block_size) must be in [0, num_blocks).
+ *   seq_lens     device int32 [B], each in [0, max_blocks_per_seq*block_size].
+ *                A sequence of length 0 gets out = 0.
+ *   num_splits   1..64: each sequence's blocks are cut into num_splits
+ *                contiguous ranges of ceil(blocks/num_splits) blocks.
+ *   scale        finite, > 0 (1/sqrt(d) for standard attention).
+ *   out          [B,Hq,d] bf16, written.
+ *   workspace    at least fa_decode_workspace_bytes(B,Hq,d,num_splits) bytes.
+ */
+int fa_decode_paged(int B, int Hq, int Hkv, int d,
+                    const void *q, const void *k_cache, const void *v_cache,
+                    int num_blocks, int block_size,
+                    const int32_t *block_table, int max_blocks_per_seq,
+                    const int32_t *seq_lens, int num_splits, float scale,
+                    void *out, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

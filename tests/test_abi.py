@@ -1,0 +1,110 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/fa355.h declares, and rejects invalid arguments before launching
+anything.  No call here reaches a kernel launch (every call is invalid by
+construction), so these run without a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_io_aware_15_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa355.h")
+
+FAKE = ctypes.c_void_p(0x1000)   # non-null, never dereferenced by validation
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.skip("libfa355.so not built")
+    return _lib.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in range(-5, 1):
+        s = lib.fa_status_str(code).decode()
+        assert s.startswith(_lib.STATUS[code])
+    assert b"unknown" in lib.fa_status_str(42)
+
+
+def _fwd(lib, dtype=1, B=1, H=1, N=16, d=64, q=FAKE, m=NULL, l=NULL,
+         scale=0.125):
+    return lib.fa_fwd(dtype, B, H, N, d, q, FAKE, FAKE, FAKE, m, l, NULL, 0,
+                      scale, NULL)
+
+
+def test_fwd_validation(lib):
+    assert _fwd(lib, q=NULL) == -1
+    assert _fwd(lib, m=FAKE) == -1            # m without l
+    assert _fwd(lib, N=0) == -2
+    assert _fwd(lib, B=0) == -2
+    assert _fwd(lib, N=(1 << 20) + 1) == -2
+    assert _fwd(lib, B=1 << 16, H=1 << 10, N=1 << 10) == -2   # > 2^31 rows
+    assert _fwd(lib, scale=0.0) == -2
+    assert _fwd(lib, scale=float("nan")) == -2
+    assert _fwd(lib, scale=float("inf")) == -2
+    assert _fwd(lib, d=96) == -3
+    assert _fwd(lib, dtype=7) == -3
+
+
+def test_bwd_workspace_and_validation(lib):
+    ws = lib.fa_bwd_workspace_bytes(2, 3, 100, 64)
+    rows = 2 * 3 * 100
+    up = lambda x: (x + 255) // 256 * 256   # noqa: E731
+    assert ws == up(rows * 64 * 4) + 2 * up(rows * 4)
+    assert lib.fa_bwd_workspace_bytes(2, 3, 100, 80) == 0
+    assert lib.fa_bwd_workspace_bytes(0, 3, 100, 64) == 0
+
+    def call(ws_ptr=FAKE, ws_bytes=ws, d=64, q=FAKE, N=100, scale=0.125):
+        return lib.fa_bwd(2, 3, N, d, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          NULL, 1, scale, FAKE, FAKE, FAKE, ws_ptr, ws_bytes,
+                          NULL)
+    assert call(q=NULL) == -1
+    assert call(N=0) == -2
+    assert call(scale=-1.0) == -2
+    assert call(d=32) == -3
+    assert call(ws_ptr=NULL) == -4
+    assert call(ws_bytes=ws - 1) == -4
+    assert call(ws_ptr=ctypes.c_void_p(0x1008)) == -4   # not 256-aligned
+
+
+def test_decode_workspace_and_validation(lib):
+    ws = lib.fa_decode_workspace_bytes(16, 32, 128, 8)
+    parts = 16 * 32 * 8
+    up = lambda x: (x + 255) // 256 * 256   # noqa: E731
+    assert ws == 2 * up(parts * 4) + up(parts * 128 * 4)
+    assert lib.fa_decode_workspace_bytes(16, 32, 128, 0) == 0
+    assert lib.fa_decode_workspace_bytes(16, 32, 128, 65) == 0
+
+    def call(Hq=32, Hkv=8, d=128, bs=16, splits=8, ws_bytes=ws, q=FAKE,
+             nb=100, scale=0.1):
+        return lib.fa_decode_paged(16, Hq, Hkv, d, q, FAKE, FAKE, nb, bs,
+                                   FAKE, 512, FAKE, splits, scale, FAKE,
+                                   FAKE, ws_bytes, NULL)
+    assert call(q=NULL) == -1
+    assert call(Hkv=7) == -2             # 32 % 7 != 0
+    assert call(nb=0) == -2
+    assert call(splits=0) == -2
+    assert call(scale=0.0) == -2
+    assert call(Hq=64, Hkv=2) == -3      # group of 32 > 16
+    assert call(d=96) == -3
+    assert call(bs=32) == -3
+    assert call(ws_bytes=ws - 4) == -4
