@@ -139,6 +139,7 @@ int fa_decode_paged(int B, int Hq, int Hkv, int d, const void *q,
   a.part_l = (float *)(ws + align_up(parts * sizeof(float)));
   a.part_o = (float *)(ws + 2 * align_up(parts * sizeof(float)));
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
   a.num_splits = num_splits;
   a.scale = scale;
   a.c = (float)((double)scale * 1.4426950408889634);

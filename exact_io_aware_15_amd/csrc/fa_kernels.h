@@ -45,7 +45,7 @@ struct DecodeArgs {
   uint16_t *out;                // [B,Hq,d]
   float *part_m, *part_l;       // [B,Hq,S]
   float *part_o;                // [B,Hq,S,d]
-  int B, Hq, Hkv, max_blocks, num_splits;
+  int B, Hq, Hkv, max_blocks, num_blocks, num_splits;
   float scale, c;
 };
 

@@ -139,7 +139,9 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
  *                may hold anything, NaN included).
  *   block_size   tokens per block; 16.
  *   block_table  device int32 [B, max_blocks_per_seq]; entries for t <
- *                ceil(seq_len/block_size) must be in [0, num_blocks).
+ *                ceil(seq_len/block_size) must be in [0, num_blocks).  An
+ *                entry outside that range is skipped (its tokens are treated
+ *                as masked) rather than read.
  *   seq_lens     device int32 [B], each in [0, max_blocks_per_seq*block_size].
  *                A sequence of length 0 gets out = 0.
  *   num_splits   1..64: each sequence's blocks are cut into num_splits
