@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Throughput of exact attention (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-sweep] [--no-cpu-baseline]
+
+A step is one forward and one backward pass (fa_fwd, then fa_bwd on its O, m,
+l) over one batch of the workload, inputs resident in HBM.  The default
+workload is the GPT-2-medium-shaped causal layer at N=4096 (B=2, H=16, d=64,
+bf16).  The printed JSON line reports:
+
+  value        (fwd + bwd algorithmic FLOPs) / time per step, in TFLOP/s;
+               forward FLOPs are 4*B*H*N^2*d (halved when causal), backward
+               2.5x that.
+  roofline     the dominant call of the step (the one with the larger mean
+               duration), timed with HIP events on the stream it runs on,
+               against MI355X's dense bf16 MFMA peak (2500 TFLOP/s); traffic
+               is the HBM bytes read + written per call from rocprofv3
+               counters (scaled by a plain copy's counter reading), or null
+               when the kernels changed after the counters were taken.
+  cpu_baseline the fp64 oracle on a bounded sample of the same workload, on
+               this host's cores (a reported baseline, not a target).
+  sweep        the other workloads: forward / backward TFLOP/s and the paged
+               decode's bandwidth against 8 TB/s.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def source_hash():
+    """Hash of the kernel sources: counters are valid only for this hash."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_io_aware_15_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2_medium_causal_4k")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+class Attn:
+    """Device-resident inputs of one attention workload, and its step."""
+
+    def __init__(self, w):
+        import torch
+        import exact_io_aware_15_amd as fa
+        from workloads import to_device
+        self.w, self.fa, self.torch = w, fa, torch
+        q, k, v = w.qkv()
+        self.q, self.k, self.v = (to_device(t) for t in (q, k, v))
+        self.do = to_device(w.dout())
+        kl = w.kv_len()
+        self.kv_len = None if kl is None else torch.from_numpy(kl).cuda()
+        self.ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d),
+                              dtype=torch.uint8, device="cuda")
+
+    def fwd(self):
+        return self.fa.fwd(self.q, self.k, self.v, causal=self.w.causal,
+                           kv_len=self.kv_len)
+
+    def bwd(self, o, m, l):
+        return self.fa.bwd(self.q, self.k, self.v, o, self.do, m, l,
+                           causal=self.w.causal, kv_len=self.kv_len,
+                           workspace=self.ws)
+
+
+def time_step(attn, steps, warmup, backward=True):
+    """Run warmup steps, then `steps` timed steps with events around each
+    forward and backward call; returns mean ms of step, fwd and bwd."""
+    torch = attn.torch
+    for _ in range(warmup):
+        o, m, l = attn.fwd()
+        if backward:
+            attn.bwd(o, m, l)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        o, m, l = attn.fwd()
+        ev[i][1].record()
+        if backward:
+            attn.bwd(o, m, l)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps if backward \
+        else 0.0
+    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
+    return step_ms, fwd_ms, bwd_ms, wall
+
+
+def decode_bench(steps, warmup):
+    import numpy as np
+    import torch
+    import exact_io_aware_15_amd as fa
+    from workloads import to_device
+    from workloads import WORKLOADS
+    w = WORKLOADS["paged_gqa_decode"]
+    q, cache = w.decode_inputs(poison_tails=False)
+    qd = to_device(q)
+    kc, vc = to_device(cache.k_cache), to_device(cache.v_cache)
+    table = torch.from_numpy(cache.block_table).cuda()
+    lens = torch.from_numpy(cache.seq_lens).cuda()
+    ws = torch.empty(fa.decode_workspace_bytes(w.B, w.H, w.d, w.splits),
+                     dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        fa.decode_paged(qd, kc, vc, table, lens, w.splits, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    e0.record()
+    for _ in range(steps):
+        fa.decode_paged(qd, kc, vc, table, lens, w.splits, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    total_len = int(np.sum(cache.seq_lens))
+    # K and V rows read: len * Hkv * d * 2 bytes each
+    kv_bytes = total_len * w.Hkv * w.d * 2 * 2
+    return {"workload": w.name, "ms": round(ms, 4),
+            "kv_bytes": kv_bytes,
+            "GB/s": round(kv_bytes / ms / 1e6, 1),
+            "frac_of_hbm_peak": round(kv_bytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+
+def sweep(steps, warmup):
+    from workloads import WORKLOADS
+    out = {}
+    for name in ["bert_large_padded", "gpt2_medium_causal_1k",
+                 "long_causal_16k_d128", "long_causal_64k_d64"]:
+        w = WORKLOADS[name]
+        attn = Attn(w)
+        step_ms, fwd_ms, bwd_ms, _ = time_step(attn, steps, warmup,
+                                               backward=w.backward)
+        r = {"fwd_ms": round(fwd_ms, 4),
+             "fwd_tflops": round(w.fwd_flops() / fwd_ms / 1e9, 1)}
+        r["fwd_frac"] = round(r["fwd_tflops"] / PEAK_BF16_TFLOPS, 4)
+        if w.backward:
+            r["bwd_ms"] = round(bwd_ms, 4)
+            r["bwd_tflops"] = round(w.bwd_flops() / bwd_ms / 1e9, 1)
+            r["bwd_frac"] = round(r["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)
+        out[name] = r
+        del attn
+    out["paged_gqa_decode"] = decode_bench(max(steps, 20), warmup)
+    return out
+
+
+def cpu_baseline(w, budget_s):
+    """fp64 oracle forward + backward on whole heads of the workload until
+    about budget_s seconds have been spent; TFLOP/s at the workload's
+    algorithmic FLOP count per head."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    q, k, v = w.qkv()
+    do = w.dout()
+    kl = w.kv_len()
+    per_head = (w.fwd_flops() + w.bwd_flops()) / (w.B * w.H)
+    t0 = time.perf_counter()
+    heads = 0
+    while True:
+        b, h = divmod(heads % (w.B * w.H), w.H)
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        klb = None if kl is None else kl[b:b + 1]
+        oracle.attention_fwd(q.exact[sl], k.exact[sl], v.exact[sl], None,
+                             w.causal, klb)
+        oracle.attention_bwd(q.exact[sl], k.exact[sl], v.exact[sl],
+                             do.exact[sl], None, w.causal, klb)
+        heads += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or heads >= w.B * w.H:
+            break
+    return {"value": round(per_head * heads / el / 1e12, 6),
+            "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle fwd+bwd on {heads} of {w.B * w.H} heads "
+                      f"of {w.name} ({el:.1f} s)"}
+
+
+def traffic_for(call):
+    """HBM bytes per call from the committed counter summary, if it was
+    taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("calls", {}).get(call)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the attention kernels shard over independent (batch, head) "
+              "units, and a multi-GPU run is not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from workloads import WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    attn = Attn(w)
+    step_ms, fwd_ms, bwd_ms, wall_ms = time_step(attn, args.steps,
+                                                 args.warmup)
+    flops = w.fwd_flops() + w.bwd_flops()
+    value = flops / step_ms / 1e9
+    if bwd_ms >= fwd_ms:
+        call, dur, cflops = "fa_bwd", bwd_ms, w.bwd_flops()
+        kern = "fa_bwd (bwd_pre + bwd_main + bwd_dq_convert launches)"
+    else:
+        call, dur, cflops = "fa_fwd", fwd_ms, w.fwd_flops()
+        kern = "fa_fwd (fwd_bf16_kernel)"
+    achieved = cflops / dur / 1e9
+    line = {
+        "metric": "attention fwd+bwd TFLOP/s (1 GPU)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, no datasets or weights)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N,
+                   "d": w.d, "causal": w.causal, "dtype": w.dtype,
+                   "fwd_flops": w.fwd_flops(), "bwd_flops": w.bwd_flops()},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd": {"ms": round(fwd_ms, 4),
+                "tflops": round(w.fwd_flops() / fwd_ms / 1e9, 1)},
+        "bwd": {"ms": round(bwd_ms, 4),
+                "tflops": round(w.bwd_flops() / bwd_ms / 1e9, 1)},
+        "host_wall_ms_per_step": round(wall_ms, 4),
+        "roofline": {"kernel": kern, "bound": "mfma",
+                     "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for(call)},
+        "kernel_source_hash": source_hash(),
+    }
+    del attn
+    if not args.no_sweep:
+        line["sweep"] = sweep(max(10, args.steps // 2), args.warmup)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -12,13 +12,7 @@ BF16_TOL = (2e-2, 1e-2)
 F32_TOL = (1e-5, 1e-5)
 
 
-def to_device(t, device="cuda"):
-    """workloads.Tensor -> torch tensor on the GPU with the stored bits."""
-    import torch
-    if t.dtype == "bf16":
-        x = torch.from_numpy(np.ascontiguousarray(t.store).view(np.int16))
-        return x.view(torch.bfloat16).to(device)
-    return torch.from_numpy(np.ascontiguousarray(t.store)).to(device)
+from workloads import to_device  # noqa: F401  (re-exported for the tests)
 
 
 def to_numpy64(x):

@@ -42,6 +42,15 @@ def bf16_value(bits):
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
+def to_device(t, device="cuda"):
+    """Copy a generated Tensor to a torch GPU tensor with the same bits."""
+    import torch
+    if t.dtype == "bf16":
+        x = torch.from_numpy(np.ascontiguousarray(t.store).view(np.int16))
+        return x.view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(t.store)).to(device)
+
+
 @dataclass
 class Tensor:
     """A generated tensor: storage bits (bf16) or fp32 data, plus exact fp64."""
