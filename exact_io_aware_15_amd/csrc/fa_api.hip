@@ -63,7 +63,7 @@ int fa_fwd(int dtype, int B, int H, int N, int d, const void *q,
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (!attn_shape_ok(B, H, N) || (d != 64 && d != 128)) return 0;
   const size_t rows = (size_t)B * H * N;
-  return align_up(rows * d * sizeof(float)) + 2 * align_up(rows * sizeof(float));
+  return 2 * align_up(rows * sizeof(float));
 }
 
 int fa_bwd(int B, int H, int N, int d, const void *q, const void *k,
@@ -85,10 +85,8 @@ int fa_bwd(int B, int H, int N, int d, const void *q, const void *k,
   a.dout = (const uint16_t *)dout; a.m = m; a.l = l; a.kv_len = kv_len;
   a.dq = (uint16_t *)dq; a.dk = (uint16_t *)dk; a.dv = (uint16_t *)dv;
   char *ws = (char *)workspace;
-  a.dq_acc = (float *)ws;
-  a.lse2 = (float *)(ws + align_up(rows * d * sizeof(float)));
-  a.delta = (float *)(ws + align_up(rows * d * sizeof(float)) +
-                      align_up(rows * sizeof(float)));
+  a.lse2 = (float *)ws;
+  a.delta = (float *)(ws + align_up(rows * sizeof(float)));
   a.B = B; a.H = H; a.N = N; a.BH = B * H;
   a.scale = scale;
   a.c = (float)((double)scale * 1.4426950408889634);

@@ -75,4 +75,44 @@ __device__ __forceinline__ u32x4 ldg128(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// Row order of a 32-row block of an MFMA operand tile held in LDS: storage
+// row p holds logical row row_perm(p) (bits 2 and 3 exchanged; the map is its
+// own inverse).  With the C-operand row order 8*(r/4)+4h+r%4, a product whose
+// A-operand rows are stored this way leaves logical row 16*(r/8)+8*h+(r%8) in
+// register r of lane half h: eight consecutive registers hold eight
+// consecutive logical rows, i.e. exactly the (h, e) contraction slots of a
+// following MFMA that consumes those registers as an operand.
+__device__ __forceinline__ int row_perm(int p) {
+  return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
+}
+
+// Transposed MFMA fragment from a row-major bf16 tile in LDS, with the tile's
+// rows in row_perm order within each 32-row block.  Returns, for lane l, the
+// 8 values T[kbase + 8*h + e][cbase + l%32] (e = 0..7, h = l/32): the operand
+// of a product that contracts over the tile's rows (V^T P^T, dS^T Q, ...).
+// Uses ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i%4 of the 8-byte chunk addressed by lane 4*e + i/4, for e = 0..3.  So source
+// lane 4*e + j points at row (kbase + 8*h + e [+4]), columns cbase + 16*(g%2)
+// + 4*j, where g = l/16.
+__device__ __forceinline__ bf16x8 lds_tr_frag(const uint16_t *tile, int pitch,
+                                              int kbase, int cbase) {
+  typedef short shortx4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, t = lane & 15;
+  const int h = g >> 1;
+  const int esrc = t >> 2, j = t & 3;
+  const int col = cbase + 16 * (g & 1) + 4 * j;
+  const int k0 = kbase + 8 * h + esrc;
+  const int k1 = k0 + 4;
+  const int r0 = (k0 & ~31) | row_perm(k0 & 31);
+  const int r1 = (k1 & ~31) | row_perm(k1 & 31);
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4 *)(tile + r0 * pitch + col));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4 *)(tile + r1 * pitch + col));
+  typedef short shortx8 __attribute__((ext_vector_type(8)));
+  const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 }  // namespace fa355

@@ -27,7 +27,6 @@ struct BwdArgs {
   const float *m, *l;                    // [B,H,N]
   const int32_t *kv_len;                 // [B] or null
   uint16_t *dq, *dk, *dv;                // [B,H,N,d] bf16
-  float *dq_acc;                         // [B,H,N,d] fp32 workspace
   float *lse2;                           // [B,H,N] workspace: log2-domain row offset
   float *delta;                          // [B,H,N] workspace: rowsum(dO*O)
   int B, H, N, BH;

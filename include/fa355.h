@@ -82,9 +82,10 @@ int fa_fwd(int dtype, int B, int H, int N, int d,
            void *stream);
 
 /*
- * fa_bwd_workspace_bytes -- device workspace fa_bwd needs for this shape:
- * an fp32 dQ accumulator [B,H,N,d] plus two fp32 row vectors [B,H,N].
- * Returns 0 for invalid sizes.
+ * fa_bwd_workspace_bytes -- device workspace fa_bwd needs for this shape: two
+ * fp32 row vectors [B,H,N] (D = rowsum(dO * O) and the log2-domain row
+ * offset m*log2(e) + log2(l)), each padded to 256 bytes.  Returns 0 for
+ * invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
