@@ -38,9 +38,17 @@ def hipcc():
     return path
 
 
+# Kernel sources may assume NaN-free score arithmetic (infinities are still
+# honoured, so -inf masking is exact): this lets max() skip canonicalising
+# MFMA results.  The API source validates arguments with isfinite() and is
+# compiled without it.
+KERNEL_FLAGS = ["-fno-honor-nans"]
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + FLAGS + ["-c", src, "-o", obj]
+    extra = [] if os.path.basename(src) == "fa_api.hip" else KERNEL_FLAGS
+    cmd = [hipcc()] + FLAGS + extra + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

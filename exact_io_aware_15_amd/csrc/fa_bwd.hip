@@ -62,42 +62,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   }
 }
 
-// Copies rows [row0, row0 + ROWS) of a [N, D] bf16 matrix into an LDS tile in
-// row_perm order (rows at or past `valid` become zero).
-template <int D, int ROWS>
-__device__ __forceinline__ void stage_rows(uint16_t *tile, int pitch,
-                                           const uint16_t *src, int row0,
-                                           int valid) {
-  constexpr int CPR = D / 8;
-  constexpr int CH = ROWS * CPR / 256;
-  static_assert(CH >= 1, "tile too small");
-  u32x4 x[CH];
-#pragma unroll
-  for (int u = 0; u < CH; ++u) {
-    const int ci = threadIdx.x + 256 * u;
-    const int row = ci / CPR, cc = ci % CPR;
-    x[u] = u32x4{0u, 0u, 0u, 0u};
-    if (row0 + row < valid) x[u] = ldg128(src + (size_t)(row0 + row) * D + cc * 8);
-  }
-#pragma unroll
-  for (int u = 0; u < CH; ++u) {
-    const int ci = threadIdx.x + 256 * u;
-    const int row = ci / CPR, cc = ci % CPR;
-    const int prow = (row & ~31) | row_perm(row & 31);
-    *reinterpret_cast<u32x4 *>(&tile[prow * pitch + cc * 8]) = x[u];
-  }
-}
-
 template <int D, bool CAUSAL, bool PADDED>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     BwdArgs a) {
   constexpr int BC = 128;    // keys per workgroup, 32 per wave
   constexpr int BR = 64;     // queries per step
-  constexpr int QP = D + 8;  // LDS row pitch (bf16)
   constexpr int CPR = D / 8;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BR * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[BR * QP];
-  __shared__ float L2s[BR], Dls[BR];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BR * D];
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BR * D];
+  __shared__ float L2s[2][BR], Dls[2][BR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -157,16 +130,38 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   const float c = a.c;
   const int q_begin = CAUSAL ? j0 : 0;
 
-  for (int q0 = q_begin; q0 < N; q0 += BR) {
-    __syncthreads();  // the previous block's operands are no longer in use
-    stage_rows<D, BR>(Qs, QP, qg, q0, N);
-    stage_rows<D, BR>(dOs, QP, dog, q0, N);
+  // Double-buffered Q / dO blocks (DMA) and their row statistics; rows past
+  // N read row N-1 and get lse2 = +inf, so their P is exactly 0.
+  auto load_stats = [&](int q0, float &lv, float &dv2) {
+    const bool ok = q0 + tid < N;
+    lv = ok ? lse2[q0 + tid] : INFINITY;
+    dv2 = ok ? dlt[q0 + tid] : 0.f;
+  };
+  float l_nx = 0.f, d_nx = 0.f;
+  if (q_begin < N) {
+    dma_tile<D, BR>(Qs[0], qg, q_begin, N - 1);
+    dma_tile<D, BR>(dOs[0], dog, q_begin, N - 1);
     if (tid < BR) {
-      const bool ok = q0 + tid < N;
-      L2s[tid] = ok ? lse2[q0 + tid] : INFINITY;
-      Dls[tid] = ok ? dlt[q0 + tid] : 0.f;
+      load_stats(q_begin, l_nx, d_nx);
+      L2s[0][tid] = l_nx;
+      Dls[0][tid] = d_nx;
     }
-    __syncthreads();
+  }
+  wait_dma();
+  __syncthreads();
+
+  int buf = 0;
+  for (int q0 = q_begin; q0 < N; q0 += BR, buf ^= 1) {
+    const bool has_next = q0 + BR < N;
+    if (has_next) {  // the other buffers were last read before the barrier
+      dma_tile<D, BR>(Qs[buf ^ 1], qg, q0 + BR, N - 1);
+      dma_tile<D, BR>(dOs[buf ^ 1], dog, q0 + BR, N - 1);
+      if (tid < BR) load_stats(q0 + BR, l_nx, d_nx);
+    }
+    const uint16_t *Qt = Qs[buf];
+    const uint16_t *dOt = dOs[buf];
+    const float *L2t = L2s[buf];
+    const float *Dlt = Dls[buf];
 
 #pragma unroll
     for (int qb = 0; qb < BR / 32; ++qb) {
@@ -177,11 +172,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const int off = (32 * qb + ln) * QP + ks * 16 + 8 * hh;
-        const u32x4 qf = *reinterpret_cast<const u32x4 *>(&Qs[off]);
-        const u32x4 df = *reinterpret_cast<const u32x4 *>(&dOs[off]);
-        s = mfma32(__builtin_bit_cast(bf16x8, qf), kb[ks], s);
-        dp = mfma32(__builtin_bit_cast(bf16x8, df), vb[ks], dp);
+        const bf16x8 qf = lds_row_frag<D>(Qt, 32 * qb + ln, ks * 16 + 8 * hh);
+        const bf16x8 df = lds_row_frag<D>(dOt, 32 * qb + ln, ks * 16 + 8 * hh);
+        s = mfma32(qf, kb[ks], s);
+        dp = mfma32(df, vb[ks], dp);
       }
       // Register r holds query qs + 16*(r/8) + 8*hh + (r%8) of this key.
       const bool need_mask =
@@ -194,13 +188,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         for (int t = 0; t < 2; ++t) {
           const int r = 2 * i + t;
           const int qo = 32 * qb + 16 * (r >> 3) + 8 * hh + (r & 7);
-          float p = fast_exp2(fmaf(s[r], c, -L2s[qo]));
+          float p = fast_exp2(fmaf(s[r], c, -L2t[qo]));
           if (need_mask) {
             const bool masked = key >= kv_valid || (CAUSAL && key > q0 + qo);
             p = masked ? 0.f : p;
           }
           pv[t] = p;
-          dsv[t] = p * (dp[r] - Dls[qo]);
+          dsv[t] = p * (dp[r] - Dlt[qo]);
         }
         pp[i] = pack_bf16x2(pv[0], pv[1]);
         ps[i] = pack_bf16x2(dsv[0], dsv[1]);
@@ -215,13 +209,19 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                           ps[4 * s2 + 3]};
 #pragma unroll
         for (int cb = 0; cb < D / 32; ++cb) {
-          const bf16x8 dof = lds_tr_frag(dOs, QP, 32 * qb + 16 * s2, cb * 32);
-          const bf16x8 qtf = lds_tr_frag(Qs, QP, 32 * qb + 16 * s2, cb * 32);
+          const bf16x8 dof = lds_tr_frag<D>(dOt, 32 * qb + 16 * s2, cb * 32);
+          const bf16x8 qtf = lds_tr_frag<D>(Qt, 32 * qb + 16 * s2, cb * 32);
           dv[cb] = mfma32(__builtin_bit_cast(bf16x8, pa), dof, dv[cb]);
           dk[cb] = mfma32(__builtin_bit_cast(bf16x8, sa), qtf, dk[cb]);
         }
       }
     }
+    if (has_next && tid < BR) {
+      L2s[buf ^ 1][tid] = l_nx;
+      Dls[buf ^ 1][tid] = d_nx;
+    }
+    wait_dma();
+    __syncthreads();
   }
 
   // Epilogue: dK = scale * dK_acc, dV; lane = column, registers = key rows.
@@ -245,9 +245,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(
     BwdArgs a) {
   constexpr int BR = 128;    // queries per workgroup, 32 per wave
   constexpr int BC = 64;     // keys per tile
-  constexpr int KP = D + 8;  // LDS row pitch (bf16)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BC * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -295,61 +294,73 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(
     for (int r = 0; r < 16; ++r) dq[cb][r] = 0.f;
   const float c = a.c;
 
+  // Double-buffered K / V tiles (DMA); keys past kv_valid read the last
+  // valid key (finite data that the mask excludes).
+  if (ntiles > 0) {
+    dma_tile<D, BC>(Ks[0], kg, 0, kv_valid - 1);
+    dma_tile<D, BC>(Vs[0], vg, 0, kv_valid - 1);
+  }
+  wait_dma();
+  __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BC;
-    __syncthreads();
-    stage_rows<D, BC>(Ks, KP, kg, k0, kv_valid);
-    stage_rows<D, BC>(Vs, KP, vg, k0, kv_valid);
-    __syncthreads();
-    if (CAUSAL && k0 > qw + 31) continue;  // tile entirely above the diagonal
-
-    uint32_t ps[2][8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const int off = (32 * kb + ln) * KP + ks * 16 + 8 * hh;
-        const u32x4 kf = *reinterpret_cast<const u32x4 *>(&Ks[off]);
-        const u32x4 vf = *reinterpret_cast<const u32x4 *>(&Vs[off]);
-        s = mfma32(__builtin_bit_cast(bf16x8, kf), qf[ks], s);
-        dp = mfma32(__builtin_bit_cast(bf16x8, vf), df[ks], dp);
-      }
-      // Register r holds key k0 + 32*kb + 16*(r/8) + 8*hh + (r%8).
-      const bool need_mask =
-          (k0 + BC > kv_valid) || (CAUSAL && k0 + BC - 1 > qw);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float dsv[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int r = 2 * i + u;
-          float p = fast_exp2(fmaf(s[r], c, -lrow));
-          if (need_mask) {
-            const int kk = k0 + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
-            const bool masked = kk >= kv_valid || (CAUSAL && kk > qi);
-            p = masked ? 0.f : p;
-          }
-          dsv[u] = p * (dp[r] - drow);
-        }
-        ps[kb][i] = pack_bf16x2(dsv[0], dsv[1]);
-      }
+    const int buf = t & 1;
+    if (t + 1 < ntiles) {  // the other buffer was last read before the barrier
+      dma_tile<D, BC>(Ks[buf ^ 1], kg, k0 + BC, kv_valid - 1);
+      dma_tile<D, BC>(Vs[buf ^ 1], vg, k0 + BC, kv_valid - 1);
     }
-    // dQ^T += K^T dS^T: A = transposed K fragments, B = this lane's dS^T.
+    const uint16_t *Kt = Ks[buf];
+    const uint16_t *Vt = Vs[buf];
+    if (!(CAUSAL && k0 > qw + 31)) {  // else: tile above the diagonal
+      uint32_t ps[2][8];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 s, dp;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const u32x4 sb = {ps[kb][4 * s2], ps[kb][4 * s2 + 1],
-                          ps[kb][4 * s2 + 2], ps[kb][4 * s2 + 3]};
+        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb) {
-          const bf16x8 ktf = lds_tr_frag(Ks, KP, 32 * kb + 16 * s2, cb * 32);
-          dq[cb] = mfma32(ktf, __builtin_bit_cast(bf16x8, sb), dq[cb]);
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const bf16x8 kf = lds_row_frag<D>(Kt, 32 * kb + ln, ks * 16 + 8 * hh);
+          const bf16x8 vf = lds_row_frag<D>(Vt, 32 * kb + ln, ks * 16 + 8 * hh);
+          s = mfma32(kf, qf[ks], s);
+          dp = mfma32(vf, df[ks], dp);
+        }
+        // Register r holds key k0 + 32*kb + 16*(r/8) + 8*hh + (r%8).
+        const bool need_mask =
+            (k0 + BC > kv_valid) || (CAUSAL && k0 + BC - 1 > qw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float dsv[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r = 2 * i + u;
+            float p = fast_exp2(fmaf(s[r], c, -lrow));
+            if (need_mask) {
+              const int kk = k0 + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
+              const bool masked = kk >= kv_valid || (CAUSAL && kk > qi);
+              p = masked ? 0.f : p;
+            }
+            dsv[u] = p * (dp[r] - drow);
+          }
+          ps[kb][i] = pack_bf16x2(dsv[0], dsv[1]);
         }
       }
+      // dQ^T += K^T dS^T: A = transposed K fragments, B = this lane's dS^T.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const u32x4 sb = {ps[kb][4 * s2], ps[kb][4 * s2 + 1],
+                            ps[kb][4 * s2 + 2], ps[kb][4 * s2 + 3]};
+#pragma unroll
+          for (int cb = 0; cb < D / 32; ++cb) {
+            const bf16x8 ktf = lds_tr_frag<D>(Kt, 32 * kb + 16 * s2, cb * 32);
+            dq[cb] = mfma32(ktf, __builtin_bit_cast(bf16x8, sb), dq[cb]);
+          }
+        }
+    }
+    wait_dma();  // the next tile has landed
+    __syncthreads();
   }
 
   if (qi < N) {

@@ -66,9 +66,21 @@ __device__ __forceinline__ float dot2_ones(uint32_t packed, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(v, one, acc, false);
 }
 
-// Value of lane (l ^ 32): exchange between the two 32-lane halves.
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+// Max / sum of x over lanes l and l ^ 32.  v_permlane32_swap(x, x) hands
+// each lane the pair {x[l], x[l ^ 32]} (lanes 0-31 get (x[l], x[l+32]),
+// lanes 32-63 get (x[l-32], x[l])), so no LDS traffic is involved.
+__device__ __forceinline__ float max_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]),
+               __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ __forceinline__ float sum_xor32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) +
+         __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
 __device__ __forceinline__ u32x4 ldg128(const void *p) {
@@ -86,16 +98,30 @@ __device__ __forceinline__ int row_perm(int p) {
   return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
 }
 
-// Transposed MFMA fragment from a row-major bf16 tile in LDS, with the tile's
-// rows in row_perm order within each 32-row block.  Returns, for lane l, the
-// 8 values T[kbase + 8*h + e][cbase + l%32] (e = 0..7, h = l/32): the operand
-// of a product that contracts over the tile's rows (V^T P^T, dS^T Q, ...).
-// Uses ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
-// i%4 of the 8-byte chunk addressed by lane 4*e + i/4, for e = 0..3.  So source
-// lane 4*e + j points at row (kbase + 8*h + e [+4]), columns cbase + 16*(g%2)
-// + 4*j, where g = l/16.
-__device__ __forceinline__ bf16x8 lds_tr_frag(const uint16_t *tile, int pitch,
-                                              int kbase, int cbase) {
+// LDS operand tiles hold rows of D bf16 with no padding; the 16-byte chunks
+// of row r are stored XOR-permuted by swz(r) = 2*(r%4) + (r/4)%2.  Eight
+// consecutive rows then put one logical chunk in eight different chunk slots
+// (a 16-byte read pass of 8 lanes touches all 32 banks once), and four
+// consecutive rows put a pair of adjacent logical chunks in four disjoint
+// slot pairs (an 8-byte transposing read pass of 16 lanes, see lds_tr_frag,
+// is conflict-free too).  Every access computes its slot from the logical
+// (row, column), so the permutation is invisible to the arithmetic.
+__device__ __forceinline__ int lds_index(int row, int col, int width) {
+  const int swz = ((row & 3) << 1) | ((row >> 2) & 1);
+  return row * width + ((((col >> 3) ^ swz)) << 3) + (col & 7);
+}
+
+// Transposed MFMA fragment from a swizzled bf16 tile in LDS (row width W),
+// whose rows are in row_perm order within each 32-row block.  Returns, for
+// lane l, the 8 values T[kbase + 8*h + e][cbase + l%32] (e = 0..7,
+// h = l/32): the operand of a product that contracts over the tile's rows
+// (V^T P^T, dS^T Q, ...).  Uses ds_read_b64_tr_b16: within each 16-lane
+// group, lane i receives element i%4 of the 8-byte chunk addressed by lane
+// 4*e + i/4, for e = 0..3.  So source lane 4*e + j points at row
+// (kbase + 8*h + e [+4]), columns cbase + 16*(g%2) + 4*j, where g = l/16.
+template <int W>
+__device__ __forceinline__ bf16x8 lds_tr_frag(const uint16_t *tile, int kbase,
+                                              int cbase) {
   typedef short shortx4 __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, t = lane & 15;
@@ -107,12 +133,62 @@ __device__ __forceinline__ bf16x8 lds_tr_frag(const uint16_t *tile, int pitch,
   const int r0 = (k0 & ~31) | row_perm(k0 & 31);
   const int r1 = (k1 & ~31) | row_perm(k1 & 31);
   const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) shortx4 *)(tile + r0 * pitch + col));
+      (__attribute__((address_space(3))) shortx4 *)(tile +
+                                                    lds_index(r0, col, W)));
   const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) shortx4 *)(tile + r1 * pitch + col));
+      (__attribute__((address_space(3))) shortx4 *)(tile +
+                                                    lds_index(r1, col, W)));
   typedef short shortx8 __attribute__((ext_vector_type(8)));
   const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// 16-byte row fragment T[row][col .. col+7] from a swizzled tile (col % 8 == 0).
+template <int W>
+__device__ __forceinline__ bf16x8 lds_row_frag(const uint16_t *tile, int row,
+                                               int col) {
+  return __builtin_bit_cast(
+      bf16x8, *reinterpret_cast<const u32x4 *>(tile + lds_index(row, col, W)));
+}
+
+// Stores a 16-byte chunk of logical row `row` (any row order) at column col.
+template <int W>
+__device__ __forceinline__ void lds_store_chunk(uint16_t *tile, int row,
+                                                int col, u32x4 x) {
+  *reinterpret_cast<u32x4 *>(tile + lds_index(row, col, W)) = x;
+}
+
+// Fills an LDS operand tile of ROWS x W bf16 (swizzled, rows in row_perm
+// order) from rows row0 .. row0+ROWS-1 of a row-major [*, W] bf16 matrix by
+// direct DMA (global_load_lds_dwordx4).  One wave instruction fills 1 KB of
+// LDS with lane i writing bytes 16i..16i+15, so each lane fetches the global
+// chunk that belongs at its slot.  Rows past last_row read row last_row
+// instead (finite data the caller masks); last_row must be >= 0.  The loads
+// complete asynchronously: wait for vmcnt(0) and a barrier before reading.
+template <int W, int ROWS>
+__device__ __forceinline__ void dma_tile(uint16_t *tile, const uint16_t *src,
+                                         int row0, int last_row) {
+  constexpr int CPR = W / 8;
+  constexpr int SEGS = ROWS * W * 2 / 1024;
+  static_assert(SEGS % 4 == 0 && ROWS % 32 == 0, "tile shape");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < SEGS / 4; ++u) {
+    const int seg = wave + 4 * u;
+    const int p = seg * 64 + lane;          // 16-byte slot in the tile
+    const int r = p / CPR, phys = p % CPR;  // storage row, chunk slot
+    const int swz = ((r & 3) << 1) | ((r >> 2) & 1);
+    const int row = min(row0 + ((r & ~31) | row_perm(r & 31)), last_row);
+    const size_t goff = (size_t)row * W + (phys ^ swz) * 8;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void *)(src + goff),
+        (__attribute__((address_space(3))) void *)(tile + seg * 512), 16, 0,
+        0);
+  }
+}
+
+__device__ __forceinline__ void wait_dma() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 }  // namespace fa355

@@ -20,28 +20,21 @@ namespace fa355 {
 
 namespace {
 
-// MFMA row p of the K operand holds key key_of_row(p) of its 32-key block
-// (bits 2 and 3 of p exchanged).  With the C-operand row order 8*(r/4)+4h+r%4
-// this puts key 16*(r/8) + 8*h + (r%8) in score register r of lane half h, so
-// each lane's eight consecutive registers are eight consecutive keys: exactly
-// the B-operand slots of the following P V MFMA, and V^T can be read with one
-// 16-byte LDS load per fragment.
-__device__ __forceinline__ int key_of_row(int p) {
-  return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
-}
+// Rescale threshold, log2 units: the accumulator keeps the running max it was
+// last rescaled to (m_ref) until a row's true max exceeds it by more than
+// this, so p = exp2(c*s - c*m_ref) stays below 2^8 while most tiles skip the
+// O *= alpha multiply.  The result is unchanged: O and l share the same
+// reference, and l is converted to the true max at the end.
+constexpr float kRescaleLog2 = 8.0f;
 
-template <int D, bool CAUSAL, bool PADDED>
+template <int D, int QPW, bool CAUSAL, bool PADDED>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
-  constexpr int BR = 128;                         // queries per workgroup
+  constexpr int QB = QPW / 32;                    // 32-query blocks per wave
+  constexpr int BR = 4 * QPW;                     // queries per workgroup
   constexpr int BC = 64;                          // keys per tile
-  constexpr int KP = D + 8;                       // K row pitch (bf16)
-  constexpr int VP = BC + 8;                      // V^T row pitch (bf16)
   constexpr int CPR = D / 8;                      // 16-byte chunks per row
-  constexpr int KCH = BC * CPR / 256;             // K chunks per thread
-  constexpr int VCH = (BC / 2) * CPR / 256;       // V row-pair chunks per thread
-  static_assert(KCH >= 1 && VCH >= 1, "tile too small for 256 threads");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -61,188 +54,186 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const uint16_t *__restrict__ vg = (const uint16_t *)a.v + hoff;
 
   const int q0 = qt * BR;
-  const int qw = q0 + wave * 32;
-  const int qi = qw + ln;
+  const int qw = q0 + wave * QPW;
   int kv_valid = N;
   if (PADDED) kv_valid = min(max(a.kv_len[b], 0), N);
   int kend = kv_valid;
   if (CAUSAL) kend = min(kend, q0 + BR);
   const int ntiles = (kend + BC - 1) / BC;
 
-  // Q as the B operand of S^T = K Q^T: lane holds Q[qi][16*ks + 8*hh + e].
-  bf16x8 qf[D / 16];
+  // Q as the B operand of S^T = K Q^T: lane holds Q[q][16*ks + 8*hh + e] for
+  // its query q = qw + 32*qb + ln of each query block.
+  bf16x8 qf[QB][D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (qi < N) x = ldg128(qg + (size_t)qi * D + ks * 16 + 8 * hh);
-    qf[ks] = __builtin_bit_cast(bf16x8, x);
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int qi = qw + 32 * qb + ln;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qi < N) x = ldg128(qg + (size_t)qi * D + ks * 16 + 8 * hh);
+      qf[qb][ks] = __builtin_bit_cast(bf16x8, x);
+    }
+
+  f32x16 oacc[QB][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][cb][r] = 0.f;
+  float m_ref[QB], m_max[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_ref[qb] = kMaxInit;  // raw (unscaled) score units
+    m_max[qb] = kMaxInit;
+    l_run[qb] = 0.f;       // over this lane's half of the keys
   }
-
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
-  float m_run = kMaxInit;  // running max of raw (unscaled) scores
-  float l_run = 0.f;       // running sum over this lane's half of the keys
   const float c = a.c;
+  const float thr = kRescaleLog2 / c;  // threshold in raw score units
 
-  u32x4 kreg[KCH];
-  u32x4 vreg[VCH][2];
-
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int ci = tid + 256 * u;
-      const int row = ci / CPR, cc = ci % CPR;
-      const int key = k0 + row;
-      kreg[u] = u32x4{0u, 0u, 0u, 0u};
-      if (key < kv_valid) kreg[u] = ldg128(kg + (size_t)key * D + cc * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int pi = tid + 256 * u;
-      const int rp = pi / CPR, cc = pi % CPR;
-      const int key = k0 + 2 * rp;
-      vreg[u][0] = u32x4{0u, 0u, 0u, 0u};
-      vreg[u][1] = u32x4{0u, 0u, 0u, 0u};
-      if (key < kv_valid) vreg[u][0] = ldg128(vg + (size_t)key * D + cc * 8);
-      if (key + 1 < kv_valid)
-        vreg[u][1] = ldg128(vg + (size_t)(key + 1) * D + cc * 8);
-    }
+  // Global -> LDS staging by direct DMA; keys past kv_valid read the last
+  // valid key instead (finite data that the mask then excludes).
+  auto load_tile = [&](int k0, int buf) {
+    dma_tile<D, BC>(Ks[buf], kg, k0, kv_valid - 1);
+    dma_tile<D, BC>(Vs[buf], vg, k0, kv_valid - 1);
   };
 
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int ci = tid + 256 * u;
-      const int row = ci / CPR, cc = ci % CPR;
-      const int prow = (row & ~31) | key_of_row(row & 31);
-      *reinterpret_cast<u32x4 *>(&Ks[prow * KP + cc * 8]) = kreg[u];
-    }
-    // V^T[c][key]: key chunks of 8 are XOR-swizzled by (c / 8) % 8 so the
-    // transposing stores and the 16-byte fragment loads avoid bank conflicts.
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int pi = tid + 256 * u;
-      const int rp = pi / CPR, cc = pi % CPR;
-      const int jc = (2 * rp) >> 3, jo = (2 * rp) & 7;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = cc * 8 + e;
-        const int jcs = jc ^ (cc & 7);
-        const uint32_t lo = (vreg[u][0][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const uint32_t hi = (vreg[u][1][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        *reinterpret_cast<uint32_t *>(&Vt[col * VP + jcs * 8 + jo]) =
-            lo | (hi << 16);
-      }
-    }
-  };
-
-  if (ntiles > 0) load_tile(0);
+  if (ntiles > 0) load_tile(0, 0);
+  wait_dma();
+  __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BC;
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(k0 + BC);  // in flight during compute
+    const int buf = t & 1;
+    // The other buffer was last read before the previous barrier.
+    if (t + 1 < ntiles) load_tile(k0 + BC, buf ^ 1);
+    const uint16_t *Kt = Ks[buf];
+    const uint16_t *Vt = Vs[buf];
 
-    if (CAUSAL && k0 > qw + 31) continue;  // tile entirely above the diagonal
-
-    f32x16 s[2];
+    if (!(CAUSAL && k0 > qw + QPW - 1)) {  // else: tile above the diagonal
+      // S^T = K Q^T for every (key block, query block).
+      f32x16 s[QB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const u32x4 kf = *reinterpret_cast<const u32x4 *>(
-            &Ks[(kb * 32 + ln) * KP + ks * 16 + 8 * hh]);
-        s[kb] = mfma32(__builtin_bit_cast(bf16x8, kf), qf[ks], s[kb]);
-      }
-    }
-
-    const bool need_mask =
-        (k0 + BC > kv_valid) || (CAUSAL && k0 + BC - 1 > qw);
-    if (need_mask) {
+          for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
-          const bool masked = key >= kv_valid || (CAUSAL && key > qi);
-          s[kb][r] = masked ? -INFINITY : s[kb][r];
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const bf16x8 kf = lds_row_frag<D>(Kt, kb * 32 + ln, ks * 16 + 8 * hh);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            s[qb][kb] = mfma32(kf, qf[qb][ks], s[qb][kb]);
         }
+
+      // Online softmax per query block.  Register r of key block kb holds
+      // key k0 + 32*kb + 16*(r/8) + 8*hh + (r%8) of this lane's query.
+      // pv[qb][kb][s2] is the B operand (8 consecutive keys) of P V.
+      u32x4 pv[QB][2][2];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qbase = qw + 32 * qb;
+        const int qi = qbase + ln;
+        const bool need_mask =
+            (k0 + BC > kv_valid) || (CAUSAL && k0 + BC - 1 > qbase);
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
+              const bool masked = key >= kv_valid || (CAUSAL && key > qi);
+              s[qb][kb][r] = masked ? -INFINITY : s[qb][kb][r];
+            }
+        }
+        float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2)
+            mx = fmaxf(mx, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
+        mx = max_xor32(mx);
+        m_max[qb] = fmaxf(m_max[qb], mx);
+        // Move the reference only when some row's max outgrew it by > thr
+        // (a wave-uniform branch; the empty asm keeps it a branch).
+        if (__any(m_max[qb] - m_ref[qb] > thr)) {
+          asm volatile("" ::: "memory");
+          const float alpha = fast_exp2((m_ref[qb] - m_max[qb]) * c);
+          m_ref[qb] = m_max[qb];
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][cb][r] *= alpha;
+        }
+        const float mc = m_ref[qb] * c;
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int r = 8 * s2 + 2 * i;
+              const float p0 = fast_exp2(fmaf(s[qb][kb][r], c, -mc));
+              const float p1 = fast_exp2(fmaf(s[qb][kb][r + 1], c, -mc));
+              pv[qb][kb][s2][i] = pack_bf16x2(p0, p1);
+              lsum = dot2_ones(pv[qb][kb][s2][i], lsum);
+            }
+        l_run[qb] += lsum;
+      }
+
+      // O^T += V^T P^T: the V^T fragment is read once (transposing LDS load)
+      // and used for every query block.  A query block whose keys are all
+      // masked contributes p = 0.
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int cb = 0; cb < D / 32; ++cb) {
+            const bf16x8 vf = lds_tr_frag<D>(Vt, kb * 32 + 16 * s2, cb * 32);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              oacc[qb][cb] = mfma32(vf, __builtin_bit_cast(bf16x8, pv[qb][kb][s2]),
+                                    oacc[qb][cb]);
+          }
     }
 
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2((m_run - m_new) * c);
-    const float mc = m_new * c;
-    m_run = m_new;
-
-    uint32_t pk[2][8];
-    float lsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float p0 = fast_exp2(fmaf(s[kb][2 * i], c, -mc));
-        const float p1 = fast_exp2(fmaf(s[kb][2 * i + 1], c, -mc));
-        pk[kb][i] = pack_bf16x2(p0, p1);
-        lsum = dot2_ones(pk[kb][i], lsum);
-      }
-    l_run = fmaf(l_run, alpha, lsum);
-
-#pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const u32x4 pb = {pk[kb][4 * s2], pk[kb][4 * s2 + 1],
-                          pk[kb][4 * s2 + 2], pk[kb][4 * s2 + 3]};
-        const int jc = kb * 4 + 2 * s2 + hh;
-#pragma unroll
-        for (int cb = 0; cb < D / 32; ++cb) {
-          const int col = cb * 32 + ln;
-          const int jcs = jc ^ ((col >> 3) & 7);
-          const u32x4 vf =
-              *reinterpret_cast<const u32x4 *>(&Vt[col * VP + jcs * 8]);
-          oacc[cb] = mfma32(__builtin_bit_cast(bf16x8, vf),
-                            __builtin_bit_cast(bf16x8, pb), oacc[cb]);
-        }
-      }
+    wait_dma();  // the next tile has landed
+    __syncthreads();
   }
 
-  // Epilogue: O = o / l (0 for a row with no visible key), m in natural units.
-  const float l_tot = l_run + xor32(l_run);
-  if (qi < N) {
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    uint16_t *og = (uint16_t *)a.o + hoff + (size_t)qi * D;
+  // Epilogue: O = o / l (0 for a row with no visible key); m in natural
+  // units and l referred to the true max.
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qi = qw + 32 * qb + ln;
+    const float l_ref = sum_xor32(l_run[qb]);
+    if (qi < N) {
+      const float inv = l_ref > 0.f ? 1.0f / l_ref : 0.f;
+      uint16_t *og = (uint16_t *)a.o + hoff + (size_t)qi * D;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c0 = cb * 32 + 8 * g + 4 * hh;
-        u32x2 w2;
-        w2[0] = pack_bf16x2(oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv);
-        w2[1] = pack_bf16x2(oacc[cb][4 * g + 2] * inv,
-                            oacc[cb][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2 *>(og + c0) = w2;
+      for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c0 = cb * 32 + 8 * g + 4 * hh;
+          u32x2 w2;
+          w2[0] = pack_bf16x2(oacc[qb][cb][4 * g] * inv,
+                              oacc[qb][cb][4 * g + 1] * inv);
+          w2[1] = pack_bf16x2(oacc[qb][cb][4 * g + 2] * inv,
+                              oacc[qb][cb][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2 *>(og + c0) = w2;
+        }
+      if (hh == 0 && a.m != nullptr) {
+        const size_t ri = (size_t)bh * N + qi;
+        const float l_true =
+            l_ref * fast_exp2((m_ref[qb] - m_max[qb]) * c);
+        a.m[ri] = l_ref > 0.f ? m_max[qb] * a.scale : -INFINITY;
+        a.l[ri] = l_ref > 0.f ? l_true : 0.f;
       }
-    if (hh == 0 && a.m != nullptr) {
-      const size_t ri = (size_t)bh * N + qi;
-      a.m[ri] = l_tot > 0.f ? m_run * a.scale : -INFINITY;
-      a.l[ri] = l_tot;
     }
   }
 }
@@ -333,14 +324,18 @@ __global__ __launch_bounds__(64, 1) void fwd_f32_kernel(FwdArgs a) {
 
 template <int D, bool CAUSAL>
 hipError_t fwd_bf16_dispatch_pad(const FwdArgs &a, hipStream_t s) {
-  const int nqt = (a.N + 127) / 128;
+  // 64 queries per wave at d = 64 (two query blocks share every K / V
+  // fragment read from LDS); 32 at d = 128, where the accumulator is twice
+  // as large.
+  constexpr int QPW = 32;
+  const int nqt = (a.N + 4 * QPW - 1) / (4 * QPW);
   dim3 grid((unsigned)(nqt * a.BH)), block(256);
   if (a.kv_len)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true>), grid, block, 0, s,
-                       a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, QPW, CAUSAL, true>), grid, block, 0,
+                       s, a);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false>), grid, block, 0, s,
-                       a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, QPW, CAUSAL, false>), grid, block,
+                       0, s, a);
   return hipGetLastError();
 }
 
