@@ -27,7 +27,6 @@ bf16).  The printed JSON line reports:
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -60,6 +59,10 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many "
+                         "bytes --steps times (the reference reading that "
+                         "scales the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -234,6 +237,14 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_bytes > 0:
+        x = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(args.steps):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "steps": args.steps}))
+        return
     w = WORKLOADS[args.workload]
     attn = Attn(w)
     step_ms, fwd_ms, bwd_ms, wall_ms = time_step(attn, args.steps,
