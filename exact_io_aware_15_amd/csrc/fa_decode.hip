@@ -29,44 +29,45 @@ namespace {
 
 constexpr int kBlock = 16;  // tokens per cache block
 
-__device__ __forceinline__ float dpp_add(float x, int ctrl_sel) {
-  int v = __builtin_bit_cast(int, x);
-  int y;
-  switch (ctrl_sel) {  // constant-folded after inlining
-    case 0: y = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); break;
-    case 1: y = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); break;
-    case 2: y = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false); break;
-    default: y = __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false); break;
+// Issues the DMA of one cache block (one KV head: 16 tokens x D) into an
+// LDS tile (rows in row_perm order, swizzled).  Slots past the sequence read
+// its last valid token instead (finite data the caller masks).
+template <int D>
+__device__ __forceinline__ void dma_block(uint16_t *tile, const uint16_t *blk,
+                                          size_t tok_stride, int n_valid) {
+  constexpr int CPR = D / 8;
+  constexpr int SEG = kBlock * D * 2 / 1024;  // 1 KB segments
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < SEG; ++i) {
+    const int p = i * 64 + lane;
+    const int r = p / CPR, phys_c = p % CPR;
+    const int swz = ((r & 3) << 1) | ((r >> 2) & 1);
+    const int tok = min(row_perm(r), n_valid - 1);
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void *)(
+            blk + (size_t)tok * tok_stride + (phys_c ^ swz) * 8),
+        (__attribute__((address_space(3))) void *)(tile + i * 512), 16, 0, 0);
   }
-  return x + __builtin_bit_cast(float, y);
 }
 
-// Sum over aligned groups of LPT lanes (LPT = 8 or 16); every lane of the
-// group receives the total.  quad_perm [1,0,3,2] and [2,3,0,1] sum quads,
-// row_half_mirror pairs the two quads of 8 lanes, row_mirror the two halves
-// of a 16-lane row.
-template <int LPT>
-__device__ __forceinline__ float group_sum(float x) {
-  x = dpp_add(x, 0);
-  x = dpp_add(x, 1);
-  x = dpp_add(x, 2);
-  if (LPT == 16) x = dpp_add(x, 3);
-  return x;
-}
+template <int D, int G, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
+  constexpr int TILE = kBlock * D;                 // bf16 per K or V tile
+  constexpr int SEG = kBlock * D * 2 / 1024;       // DMA ops per tile
+  constexpr int TCH = 256;                         // table entries per chunk
+  static_assert(G <= 32, "a query group must fit the 32 MFMA columns");
+  // Per wave: two buffers, each a K tile and a V tile.
+  __shared__ __attribute__((aligned(16))) uint16_t KVs[NW][2][2][TILE];
+  __shared__ int tab[TCH];
+  __shared__ float sm_m[NW][G], sm_l[NW][G];
+  __shared__ float sm_o[NW][G][D];
 
-template <int D, int G>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
-  constexpr int LPT = D / 8;          // lanes per token
-  constexpr int TPR = 64 / LPT;       // tokens per round per wave
-  constexpr int ROUNDS = kBlock / TPR;
-  constexpr int NST = 4 * TPR;        // partial states per workgroup
-  __shared__ float sm_m[G][NST];
-  __shared__ float sm_l[G][NST];
-  __shared__ float sm_o[G][NST][D];
-
-  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  // KV heads vary fastest: the Hkv workgroups of one (split, sequence) are
+  // dispatched together and read the same cache blocks at once.
+  const int hk = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp = lane / LPT, lig = lane % LPT;
+  const int ln = lane & 31, hh = lane >> 5;
   const int S = a.num_splits;
   const int Hkv = a.Hkv;
 
@@ -77,108 +78,140 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int t_begin = min(nblk, split * per);
   const int t_end = min(nblk, t_begin + per);
 
-  // q for the G heads of this group, pre-scaled into log2 units.
-  float qf[G][8];
+  // Scores are S^T = K Q^T on v_mfma_f32_32x32x16_bf16: MFMA rows are the
+  // block's 16 tokens (rows 16..31 are zero), columns the G query heads of
+  // this KV head's group (columns G..31 are zero).  Q as the B operand:
+  // lane = head column, slots = head dim.
+  bf16x8 qf[D / 16];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int hq = hk * G + g;
-    const u32x4 x = ldg128(a.q + ((size_t)b * a.Hq + hq) * D + lig * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      qf[g][e] = a.c * bf16_to_f32((uint16_t)(x[e >> 1] >> (16 * (e & 1))));
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (ln < G)
+      x = ldg128(a.q + ((size_t)b * a.Hq + hk * G + ln) * D + ks * 16 + 8 * hh);
+    qf[ks] = __builtin_bit_cast(bf16x8, x);
   }
 
-  float m_run[G], l_run[G], o[G][8];
+  // O^T accumulator: lane = head column, register r of cb holds head-dim row
+  // cb*32 + 8*(r/4) + 4*hh + (r%4).
+  f32x16 oacc[D / 32];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_run[g] = kMaxInit;
-    l_run[g] = 0.f;
+  for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
-  }
+    for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
+  float m_run = kMaxInit, l_run = 0.f;  // raw score units; l over this half
+  const float c = a.c;
 
   const int32_t *table = a.block_table + (size_t)b * a.max_blocks;
   const size_t tok_stride = (size_t)Hkv * D;  // elements between tokens
-  for (int t = t_begin + wave; t < t_end; t += 4) {
-    const int phys = table[t];
-    if (phys < 0 || phys >= a.num_blocks) continue;  // never read outside the cache
-    const size_t base = ((size_t)phys * kBlock * Hkv + hk) * D + lig * 8;
-    u32x4 kr[ROUNDS], vr[ROUNDS];
-    bool ok[ROUNDS];
+  const size_t head_off = (size_t)hk * D;
+
+  for (int c0 = t_begin; c0 < t_end; c0 += TCH) {
+    const int c1 = min(t_end, c0 + TCH);
+    __syncthreads();  // previous chunk's table entries are no longer read
+    for (int x = tid; x < c1 - c0; x += 64 * NW) {
+      const int ph = table[c0 + x];
+      tab[x] = (ph >= 0 && ph < a.num_blocks) ? ph : -1;  // never read outside
+    }
+    __syncthreads();
+
+    // This wave's blocks: c0 + wave, +NW, ...; block i+1's DMA is issued
+    // before block i is computed (double buffer per wave).
+    auto issue = [&](int t, int buf) {
+      const int ph = tab[t - c0];
+      if (ph < 0) return;
+      const int n_valid = min(kBlock, len - t * kBlock);  // >= 1
+      const size_t boff = (size_t)ph * kBlock * tok_stride + head_off;
+      dma_block<D>(KVs[wave][buf][0], a.k_cache + boff, tok_stride, n_valid);
+      dma_block<D>(KVs[wave][buf][1], a.v_cache + boff, tok_stride, n_valid);
+    };
+    int buf = 0;
+    int t = c0 + wave;
+    if (t < c1) issue(t, 0);
+    for (; t < c1; t += NW, buf ^= 1) {
+      const bool has_next = t + NW < c1;
+      if (has_next) {
+        issue(t + NW, buf ^ 1);
+        // wait for this block's tiles; the next block's may stay in flight
+        if (tab[t + NW - c0] >= 0)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * SEG) : "memory");
+        else
+          wait_dma();
+      } else {
+        wait_dma();
+      }
+      if (tab[t - c0] < 0) continue;
+      const int n_valid = min(kBlock, len - t * kBlock);
+      const uint16_t *Kt = KVs[wave][buf][0];
+      const uint16_t *Vt = KVs[wave][buf][1];
+      f32x16 s;
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
-      const int slot = r * TPR + grp;
-      ok[r] = t * kBlock + slot < len;
-      kr[r] = u32x4{0u, 0u, 0u, 0u};
-      vr[r] = u32x4{0u, 0u, 0u, 0u};
-      if (ok[r]) {
-        kr[r] = ldg128(a.k_cache + base + slot * tok_stride);
-        vr[r] = ldg128(a.v_cache + base + slot * tok_stride);
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        bf16x8 kf = {};
+        if (ln < kBlock) kf = lds_row_frag<D>(Kt, ln, ks * 16 + 8 * hh);
+        s = mfma32(kf, qf[ks], s);
+      }
+      // Registers 0..7 hold tokens 8*hh + r of this lane's head.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const bool ok = 8 * hh + r < n_valid;
+        s[r] = ok ? s[r] : -INFINITY;
+        mx = fmaxf(mx, s[r]);
+      }
+      const float m_new = fmaxf(m_run, max_xor32(mx));
+      const float alpha = fast_exp2((m_run - m_new) * c);
+      const float mc = m_new * c;
+      m_run = m_new;
+      u32x4 pb;
+      float lsum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = fast_exp2(fmaf(s[2 * i], c, -mc));
+        const float p1 = fast_exp2(fmaf(s[2 * i + 1], c, -mc));
+        pb[i] = pack_bf16x2(p0, p1);
+        lsum = dot2_ones(pb[i], lsum);
+      }
+      l_run = fmaf(l_run, alpha, lsum);
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+        oacc[cb] = mfma32(lds_tr_frag<D>(Vt, 0, cb * 32),
+                          __builtin_bit_cast(bf16x8, pb), oacc[cb]);
       }
     }
-    float sc[ROUNDS][G];
-#pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
-      float kf[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        kf[e] = bf16_to_f32((uint16_t)(kr[r][e >> 1] >> (16 * (e & 1))));
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(qf[g][e], kf[e], acc);
-        acc = group_sum<LPT>(acc);
-        sc[r][g] = ok[r] ? acc : -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = sc[0][g];
-#pragma unroll
-      for (int r = 1; r < ROUNDS; ++r) mx = fmaxf(mx, sc[r][g]);
-      const float m_new = fmaxf(m_run[g], mx);
-      const float alpha = fast_exp2(m_run[g] - m_new);
-      m_run[g] = m_new;
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[g][e] *= alpha;
-#pragma unroll
-      for (int r = 0; r < ROUNDS; ++r) {
-        const float p = fast_exp2(sc[r][g] - m_new);
-        ps += p;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          o[g][e] = fmaf(
-              p, bf16_to_f32((uint16_t)(vr[r][e >> 1] >> (16 * (e & 1)))),
-              o[g][e]);
-      }
-      l_run[g] = fmaf(l_run[g], alpha, ps);
-    }
+    wait_dma();
   }
 
-  // Merge the workgroup's partial states (one per wave and token group).
-  const int st = wave * TPR + grp;
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    if (lig == 0) {
-      sm_m[g][st] = m_run[g];
-      sm_l[g][st] = l_run[g];
+  // Merge the waves' states, then write the split's triple.
+  const float l_tot = sum_xor32(l_run);
+  if (ln < G) {
+    if (hh == 0) {
+      sm_m[wave][ln] = m_run;
+      sm_l[wave][ln] = l_tot;
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sm_o[g][st][lig * 8 + e] = o[g][e];
+    for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sm_o[wave][ln][cb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)] =
+            oacc[cb][r];
   }
   __syncthreads();
   const size_t pbase = ((size_t)b * a.Hq + hk * G) * S + split;
-  for (int x = tid; x < G * D; x += 256) {
+  for (int x = tid; x < G * D; x += 64 * NW) {
     const int g = x / D, col = x % D;
-    float mx = sm_m[g][0];
-    for (int s2 = 1; s2 < NST; ++s2) mx = fmaxf(mx, sm_m[g][s2]);
+    float mx = sm_m[0][g];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, sm_m[w][g]);
     float acc = 0.f, lsum = 0.f;
-    for (int s2 = 0; s2 < NST; ++s2) {
-      const float w = fast_exp2(sm_m[g][s2] - mx);
-      acc = fmaf(w, sm_o[g][s2][col], acc);
-      lsum = fmaf(w, sm_l[g][s2], lsum);
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float wt = fast_exp2((sm_m[w][g] - mx) * c);
+      acc = fmaf(wt, sm_o[w][g][col], acc);
+      lsum = fmaf(wt, sm_l[w][g], lsum);
     }
     const size_t pi = pbase + (size_t)g * S;
     a.part_o[pi * D + col] = acc;
@@ -198,7 +231,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   for (int s = 1; s < S; ++s) mx = fmaxf(mx, a.part_m[pbase + s]);
   float acc = 0.f, lsum = 0.f;
   for (int s = 0; s < S; ++s) {
-    const float w = fast_exp2(a.part_m[pbase + s] - mx);
+    const float w = fast_exp2((a.part_m[pbase + s] - mx) * a.c);
     acc = fmaf(w, a.part_o[(pbase + s) * D + col], acc);
     lsum = fmaf(w, a.part_l[pbase + s], lsum);
   }
@@ -209,8 +242,11 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
 
 template <int D, int G>
 hipError_t decode_dispatch_g(const DecodeArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_split_kernel<D, G>),
-                     dim3(a.num_splits, a.Hkv, a.B), dim3(256), 0, s, a);
+  // 8 waves per workgroup at d = 64 and for small groups at d = 128 (LDS
+  // allows it); 4 otherwise.
+  constexpr int NW = (D == 64 || G <= 4) ? 8 : 4;
+  hipLaunchKernelGGL((decode_split_kernel<D, G, NW>),
+                     dim3(a.Hkv, a.num_splits, a.B), dim3(64 * NW), 0, s, a);
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.Hq, a.B), dim3(D), 0, s,
                      a);
   return hipGetLastError();
