@@ -70,7 +70,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   constexpr int CPR = D / 8;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BR * D];
   __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BR * D];
-  __shared__ float L2s[2][BR], Dls[2][BR];
+  // Row statistics of the staged queries, interleaved (lse2, D) per query.
+  __shared__ __attribute__((aligned(16))) float LDs[2][2 * BR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -143,8 +144,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     dma_tile<D, BR>(dOs[0], dog, q_begin, N - 1);
     if (tid < BR) {
       load_stats(q_begin, l_nx, d_nx);
-      L2s[0][tid] = l_nx;
-      Dls[0][tid] = d_nx;
+      LDs[0][2 * tid] = l_nx;
+      LDs[0][2 * tid + 1] = d_nx;
     }
   }
   wait_dma();
@@ -160,8 +161,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     }
     const uint16_t *Qt = Qs[buf];
     const uint16_t *dOt = dOs[buf];
-    const float *L2t = L2s[buf];
-    const float *Dlt = Dls[buf];
+    const float *LDt = LDs[buf];
 
 #pragma unroll
     for (int qb = 0; qb < BR / 32; ++qb) {
@@ -183,18 +183,22 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
       uint32_t pp[8], ps[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        // registers 2i, 2i+1 hold two consecutive queries: one 16-byte read
+        // gives both (lse2, D) pairs
+        const int qo0 = 32 * qb + 16 * (i >> 2) + 8 * hh + 2 * (i & 3);
+        const f32x4 st = *reinterpret_cast<const f32x4 *>(&LDt[2 * qo0]);
         float pv[2], dsv[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int r = 2 * i + t;
-          const int qo = 32 * qb + 16 * (r >> 3) + 8 * hh + (r & 7);
-          float p = fast_exp2(fmaf(s[r], c, -L2t[qo]));
+          float p = fast_exp2(fmaf(s[r], c, -st[2 * t]));
           if (need_mask) {
-            const bool masked = key >= kv_valid || (CAUSAL && key > q0 + qo);
+            const bool masked =
+                key >= kv_valid || (CAUSAL && key > q0 + qo0 + t);
             p = masked ? 0.f : p;
           }
           pv[t] = p;
-          dsv[t] = p * (dp[r] - Dlt[qo]);
+          dsv[t] = p * (dp[r] - st[2 * t + 1]);
         }
         pp[i] = pack_bf16x2(pv[0], pv[1]);
         ps[i] = pack_bf16x2(dsv[0], dsv[1]);
@@ -217,8 +221,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
       }
     }
     if (has_next && tid < BR) {
-      L2s[buf ^ 1][tid] = l_nx;
-      Dls[buf ^ 1][tid] = d_nx;
+      LDs[buf ^ 1][2 * tid] = l_nx;
+      LDs[buf ^ 1][2 * tid + 1] = d_nx;
     }
     wait_dma();
     __syncthreads();
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 }
 
 template <int D, bool CAUSAL, bool PADDED>
-__global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
     BwdArgs a) {
   constexpr int BR = 128;    // queries per workgroup, 32 per wave
   constexpr int BC = 64;     // keys per tile

@@ -242,9 +242,9 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
 
 template <int D, int G>
 hipError_t decode_dispatch_g(const DecodeArgs &a, hipStream_t s) {
-  // 8 waves per workgroup at d = 64 and for small groups at d = 128 (LDS
-  // allows it); 4 otherwise.
-  constexpr int NW = (D == 64 || G <= 4) ? 8 : 4;
+  // Four waves per workgroup: two workgroups fit a CU's LDS at d = 128,
+  // and measured faster than one 8-wave workgroup.
+  constexpr int NW = 4;
   hipLaunchKernelGGL((decode_split_kernel<D, G, NW>),
                      dim3(a.Hkv, a.num_splits, a.B), dim3(64 * NW), 0, s, a);
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.Hq, a.B), dim3(D), 0, s,
