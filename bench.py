@@ -39,6 +39,41 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
+# ---------------------------------------------------------------- IO model --
+# FA notes §3.5: standard attention needs Theta(N d + N^2) HBM accesses,
+# FlashAttention Theta(N^2 d^2 / M) for on-chip memory of M elements.  The
+# bench reports both beside the measured bytes (constants dropped, per head).
+
+def standard_accesses(N, d):
+    """Theta(N d + N^2) accesses of standard attention (one head)."""
+    return N * d + N * N
+
+
+def flash_accesses(N, d, M):
+    """Theta(N^2 d^2 / M) accesses of the tiled method (one head)."""
+    return N * N * d * d / M
+
+
+def score_matrix_bytes(N, bytes_per_element, matrices=1, heads=1):
+    """Size of materialising `matrices` N x N matrices for `heads` heads."""
+    return N * N * bytes_per_element * matrices * heads
+
+
+def compulsory_bytes(w, backward):
+    """Bytes every implementation must move: inputs read once, outputs
+    written once (fwd: Q,K,V in, O out, m,l out; bwd: Q,K,V,O,dO in,
+    dQ,dK,dV out, m,l in)."""
+    s = 2 if w.dtype == "bf16" else 4
+    nd = w.B * w.H * w.N * w.d
+    rows = w.B * w.H * w.N
+    if backward:
+        return s * 8 * nd + 8 * rows
+    return s * 4 * nd + 8 * rows
+
+
+LDS_BYTES_PER_CU = 160 * 1024
+
+
 def source_hash():
     """Hash of the kernel sources: counters are valid only for this hash."""
     h = hashlib.sha256()
@@ -286,6 +321,20 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for(call)},
         "kernel_source_hash": source_hash(),
+        "io": {
+            "unit": "bytes per call",
+            "fa_bwd_measured": traffic_for("fa_bwd"),
+            "fa_bwd_compulsory": compulsory_bytes(w, True),
+            "fa_fwd_measured": traffic_for("fa_fwd"),
+            "fa_fwd_compulsory": compulsory_bytes(w, False),
+            # Theta(N^2 d^2 / M) per head x B*H heads (halved when causal),
+            # M = one CU's LDS in bf16 elements; constants dropped
+            "fwd_theta_bound": (w.B * w.H * 2 * flash_accesses(
+                w.N, w.d, LDS_BYTES_PER_CU // 2) * (0.5 if w.causal else 1)),
+            "standard_theta": w.B * w.H * 2 * standard_accesses(w.N, w.d),
+            "materialised_scores_fp32": score_matrix_bytes(
+                w.N, 4, 1, w.B * w.H),
+        },
     }
     del attn
     if not args.no_sweep:

@@ -94,3 +94,42 @@ def test_bwd_workload_4k_sampled_heads():
     do = w.dout()
     print("bwd workload gpt2_medium_causal_4k (heads 0, 9)", flush=True)
     _check(w.name, q, k, v, do, True, None, heads=[0, 9])
+
+
+def test_bwd_is_bitwise_deterministic():
+    """No atomics anywhere in the backward: two runs agree bit for bit."""
+    import torch
+    import exact_io_aware_15_amd as fa
+    q, k, v = (to_device(normal((2, 3, 300, 64), 82, t, "bf16"))
+               for t in range(3))
+    do = to_device(normal((2, 3, 300, 64), 82, TID_DO, "bf16"))
+    o, m, l = fa.fwd(q, k, v, causal=True)
+    a = fa.bwd(q, k, v, o, do, m, l, causal=True)
+    b = fa.bwd(q, k, v, o, do, m, l, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_masked_keys_never_read_into_arithmetic():
+    """Keys past kv_len hold NaN in K and V: dq equals the clean run's, and
+    dk, dv are exactly zero there."""
+    import torch
+    import exact_io_aware_15_amd as fa
+    q, k, v = (to_device(normal((2, 2, 260, 64), 83, t, "bf16"))
+               for t in range(3))
+    do = to_device(normal((2, 2, 260, 64), 83, TID_DO, "bf16"))
+    kl = torch.tensor([130, 211], dtype=torch.int32, device="cuda")
+    o, m, l = fa.fwd(q, k, v, kv_len=kl)
+    g1 = fa.bwd(q, k, v, o, do, m, l, kv_len=kl)
+    kp, vp = k.clone(), v.clone()
+    for b, L in enumerate([130, 211]):
+        kp[b, :, L:] = float("nan")
+        vp[b, :, L:] = float("nan")
+    g2 = fa.bwd(q, kp, vp, o, do, m, l, kv_len=kl)
+    torch.cuda.synchronize()
+    assert torch.equal(g1[0], g2[0])
+    for b, L in enumerate([130, 211]):
+        assert torch.all(g2[1][b, :, L:] == 0) and torch.all(g2[2][b, :, L:] == 0)
+        assert torch.equal(g1[1][b, :, :L], g2[1][b, :, :L])
+        assert torch.equal(g1[2][b, :, :L], g2[2][b, :, :L])

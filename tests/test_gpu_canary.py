@@ -1,0 +1,103 @@
+"""Out-of-bounds write checks: every output and workspace buffer is placed
+between canary regions and called directly through the C ABI; after the call
+the canaries must be untouched.  Shapes have ragged tails."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+from exact_io_aware_15_amd import _lib
+from workloads import TID_DO, normal, paged_cache, to_device
+
+pytestmark = pytest.mark.gpu
+
+PAD = 4096
+FILL = 0xA5
+
+
+class Guarded:
+    """A device buffer of `nbytes` with PAD canary bytes on each side."""
+
+    def __init__(self, nbytes):
+        import torch
+        self.n = nbytes
+        self.buf = torch.full((nbytes + 2 * PAD,), FILL, dtype=torch.uint8,
+                              device="cuda")
+
+    @property
+    def ptr(self):
+        return ctypes.c_void_p(self.buf.data_ptr() + PAD)
+
+    def intact(self):
+        import torch
+        torch.cuda.synchronize()
+        h = self.buf.cpu().numpy()
+        return bool(np.all(h[:PAD] == FILL) and np.all(h[PAD + self.n:] == FILL))
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+@pytest.mark.parametrize("dtype,d,causal,padded", [
+    ("bf16", 64, True, False), ("bf16", 128, False, True),
+    ("f32", 64, True, True)])
+def test_fwd_writes_stay_in_bounds(dtype, d, causal, padded):
+    import torch
+    B, H, N = 2, 3, 333
+    q, k, v = (to_device(normal((B, H, N, d), 84, t, dtype)) for t in range(3))
+    es = 2 if dtype == "bf16" else 4
+    o = Guarded(B * H * N * d * es)
+    m = Guarded(B * H * N * 4)
+    l = Guarded(B * H * N * 4)
+    kl = torch.tensor([N, 100], dtype=torch.int32, device="cuda")
+    st = _lib.lib().fa_fwd(1 if dtype == "bf16" else 0, B, H, N, d, _p(q),
+                           _p(k), _p(v), o.ptr, m.ptr, l.ptr,
+                           _p(kl) if padded else None, int(causal),
+                           1.0 / np.sqrt(d), _stream())
+    assert st == 0
+    assert o.intact() and m.intact() and l.intact()
+
+
+def test_bwd_writes_stay_in_bounds():
+    import torch
+    import exact_io_aware_15_amd as fa
+    B, H, N, d = 2, 2, 333, 64
+    q, k, v = (to_device(normal((B, H, N, d), 85, t, "bf16")) for t in range(3))
+    do = to_device(normal((B, H, N, d), 85, TID_DO, "bf16"))
+    kl = torch.tensor([N, 150], dtype=torch.int32, device="cuda")
+    o, m, l = fa.fwd(q, k, v, causal=True, kv_len=kl)
+    grads = [Guarded(B * H * N * d * 2) for _ in range(3)]
+    wsb = _lib.lib().fa_bwd_workspace_bytes(B, H, N, d)
+    ws = Guarded(wsb)
+    # the workspace pointer must be 256-byte aligned: PAD keeps it so
+    st = _lib.lib().fa_bwd(B, H, N, d, _p(q), _p(k), _p(v), _p(o), _p(do),
+                           _p(m), _p(l), _p(kl), 1, 0.125, grads[0].ptr,
+                           grads[1].ptr, grads[2].ptr, ws.ptr, wsb, _stream())
+    assert st == 0
+    assert all(g.intact() for g in grads) and ws.intact()
+
+
+def test_decode_writes_stay_in_bounds():
+    import torch
+    lens = [37, 300, 1, 0]
+    cache = paged_cache(lens, 2, 128, 16, 20, 86, poison_tails=True)
+    q = to_device(normal((4, 8, 128), 86, 0, "bf16"))
+    kc, vc = to_device(cache.k_cache), to_device(cache.v_cache)
+    table = torch.from_numpy(cache.block_table).cuda()
+    sl = torch.from_numpy(cache.seq_lens).cuda()
+    out = Guarded(4 * 8 * 128 * 2)
+    wsb = _lib.lib().fa_decode_workspace_bytes(4, 8, 128, 3)
+    ws = Guarded(wsb)
+    st = _lib.lib().fa_decode_paged(4, 8, 2, 128, _p(q), _p(kc), _p(vc),
+                                    kc.shape[0], 16, _p(table), 20, _p(sl), 3,
+                                    1.0 / np.sqrt(128), out.ptr, ws.ptr, wsb,
+                                    _stream())
+    assert st == 0
+    assert out.intact() and ws.intact()
