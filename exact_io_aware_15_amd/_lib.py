@@ -18,6 +18,8 @@ STATUS = {0: "FA_OK", -1: "FA_E_NULLPTR", -2: "FA_E_SHAPE",
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "fa_status_str": (ctypes.c_char_p, [_I]),
+    "fa_last_hip_error": (_I, []),
+    "fa_last_hip_error_str": (ctypes.c_char_p, []),
     "fa_fwd": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _F,
                     _P]),
     "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I]),
@@ -34,9 +36,10 @@ class LibraryMissing(RuntimeError):
 
 
 class FaError(RuntimeError):
-    def __init__(self, fn, status):
+    def __init__(self, fn, status, detail=None):
         self.status = status
-        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+        msg = f"{fn} failed: {STATUS.get(status, status)}"
+        super().__init__(msg if detail is None else f"{msg}: {detail}")
 
 
 _lib = None
@@ -61,4 +64,9 @@ def lib():
 
 def check(fn, status):
     if status != 0:
-        raise FaError(fn, status)
+        err = FaError(fn, status)
+        if status == -5 and _lib is not None:   # FA_E_HIP: add HIP's reason
+            why = _lib.fa_last_hip_error_str().decode()
+            err = FaError(fn, status, f"{why} (hipError_t "
+                                      f"{_lib.fa_last_hip_error()})")
+        raise err

@@ -24,7 +24,14 @@ bool attn_shape_ok(int B, int H, int N) {
   return (long long)B * H * N <= (1LL << 31) - 1;
 }
 
-int from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_E_HIP; }
+// The HIP error behind the calling thread's most recent FA_E_HIP.
+thread_local hipError_t last_hip_error = hipSuccess;
+
+int from_hip(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  last_hip_error = e;
+  return FA_E_HIP;
+}
 
 }  // namespace
 
@@ -40,6 +47,12 @@ const char *fa_status_str(int status) {
     case FA_E_HIP: return "FA_E_HIP: HIP runtime error at launch";
     default: return "unknown fa_status";
   }
+}
+
+int fa_last_hip_error(void) { return (int)last_hip_error; }
+
+const char *fa_last_hip_error_str(void) {
+  return hipGetErrorString(last_hip_error);
 }
 
 int fa_fwd(int dtype, int B, int H, int N, int d, const void *q,

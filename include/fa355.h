@@ -49,6 +49,15 @@ typedef enum {
 const char *fa_status_str(int status);
 
 /*
+ * fa_last_hip_error -- the hipError_t value behind the calling thread's most
+ * recent FA_E_HIP (hipSuccess = 0 if there has been none); it is not reset by
+ * later successful calls.  fa_last_hip_error_str is HIP's own text for it
+ * (static storage, never NULL).  Neither touches the device.
+ */
+int fa_last_hip_error(void);
+const char *fa_last_hip_error_str(void);
+
+/*
  * fa_fwd -- exact attention forward, O = softmax(scale * Q K^T) V.
  *
  * Computes FA notes §2.1 (standard attention) with the tiled, fused method of

@@ -108,3 +108,10 @@ def test_decode_workspace_and_validation(lib):
     assert call(d=96) == -3
     assert call(bs=32) == -3
     assert call(ws_bytes=ws - 4) == -4
+
+
+def test_last_hip_error_starts_clear(lib):
+    # Validation failures are not HIP errors and leave the record untouched.
+    assert _fwd(lib, q=NULL) == -1
+    assert lib.fa_last_hip_error() == 0
+    assert lib.fa_last_hip_error_str()
