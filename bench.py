@@ -155,7 +155,7 @@ def time_step(attn, steps, warmup, backward=True):
     return step_ms, fwd_ms, bwd_ms, wall
 
 
-def decode_bench(steps, warmup):
+def decode_bench(steps, warmup, splits=None):
     import numpy as np
     import torch
     import exact_io_aware_15_amd as fa
@@ -167,22 +167,23 @@ def decode_bench(steps, warmup):
     kc, vc = to_device(cache.k_cache), to_device(cache.v_cache)
     table = torch.from_numpy(cache.block_table).cuda()
     lens = torch.from_numpy(cache.seq_lens).cuda()
-    ws = torch.empty(fa.decode_workspace_bytes(w.B, w.H, w.d, w.splits),
+    splits = w.splits if splits is None else splits
+    ws = torch.empty(fa.decode_workspace_bytes(w.B, w.H, w.d, splits),
                      dtype=torch.uint8, device="cuda")
     for _ in range(warmup):
-        fa.decode_paged(qd, kc, vc, table, lens, w.splits, workspace=ws)
+        fa.decode_paged(qd, kc, vc, table, lens, splits, workspace=ws)
     torch.cuda.synchronize()
     e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
     e0.record()
     for _ in range(steps):
-        fa.decode_paged(qd, kc, vc, table, lens, w.splits, workspace=ws)
+        fa.decode_paged(qd, kc, vc, table, lens, splits, workspace=ws)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     total_len = int(np.sum(cache.seq_lens))
     # K and V rows read: len * Hkv * d * 2 bytes each
     kv_bytes = total_len * w.Hkv * w.d * 2 * 2
-    return {"workload": w.name, "ms": round(ms, 4),
+    return {"workload": w.name, "num_splits": splits, "ms": round(ms, 4),
             "kv_bytes": kv_bytes,
             "GB/s": round(kv_bytes / ms / 1e6, 1),
             "frac_of_hbm_peak": round(kv_bytes / ms / 1e6 / PEAK_HBM_GBS, 4)}

@@ -126,13 +126,13 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits=8,
                  scale=None, workspace=None):
     """Single-token GQA decode over a paged cache.
 
-    q: [B,Hq,d] bf16; k_cache, v_cache: [num_blocks, block_size, Hkv, d] bf16;
+    q: [B,Hq,d] bf16; k_cache, v_cache: [num_blocks, Hkv, block_size, d] bf16;
     block_table: int32 [B, max_blocks]; seq_lens: int32 [B].  Returns out
     [B,Hq,d] bf16.
     """
     torch = _torch()
     B, Hq, d = q.shape
-    nb, bs, Hkv, dk = k_cache.shape
+    nb, Hkv, bs, dk = k_cache.shape
     _check_dev("q", q, torch.bfloat16)
     _check_dev("k_cache", k_cache, torch.bfloat16)
     _check_dev("v_cache", v_cache, torch.bfloat16, k_cache.shape)

@@ -10,16 +10,16 @@
 // parallelism along queries, so the key range is split over workgroups and
 // their (m, l, o) triples are merged (FA notes §3.1 merge rule).
 //
-// Split kernel: grid (num_splits, Hkv, B), 4 waves.  Each wave walks its share
-// of the split's blocks; a block's 16 tokens are taken D/8 lanes per token
-// (one 16-byte chunk each), 64/(D/8) tokens per round.  Scores for a block are
-// reduced across the token's lanes with DPP, then one running-max update per
-// block and head.  Slots past the sequence length are never loaded: their V
-// registers hold zero and their scores -inf.  The 4 x (64/(D/8)) partial
-// states of the workgroup are merged through LDS into the split's triple.
+// Split kernel: grid (Hkv, num_splits, B), NW waves.  Wave w of a split takes
+// the split's blocks w, w + NW, ...; their table entries sit one per lane.
+// Per block, on 16 x 16 matrix-core tiles (tokens x query heads of the
+// group): S^T = K Q^T with K read straight from HBM into registers, the
+// online-softmax update per head, then O^T += V^T P^T with V staged in LDS
+// by direct DMA and read back transposed.  While a block is computed, the
+// next block's K (registers) and V (the other LDS slot) are in flight.  The
+// NW per-wave states are merged through LDS into the split's triple.
 // Merge kernel: grid (Hq, B): out = sum_p w_p o_p / sum_p w_p l_p with
-// w_p = exp2(m_p - max m).  All maxima are kept in log2 units (q is
-// pre-multiplied by scale * log2(e)).
+// w_p = exp2((m_p - max m) * scale * log2 e).
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -29,45 +29,52 @@ namespace {
 
 constexpr int kBlock = 16;  // tokens per cache block
 
-// Issues the DMA of one cache block (one KV head: 16 tokens x D) into an
-// LDS tile (rows in row_perm order, swizzled).  Slots past the sequence read
-// its last valid token instead (finite data the caller masks).
+// Issues the DMA of one block's V tile (16 tokens x D of one KV head) into
+// an LDS slot: row r holds token r, its 16-byte chunk c at position
+// c ^ swz(r).  Slots past the sequence read its last valid token instead
+// (finite data that gets probability 0).
 template <int D>
-__device__ __forceinline__ void dma_block(uint16_t *tile, const uint16_t *blk,
-                                          size_t tok_stride, int n_valid) {
+__device__ __forceinline__ void dma_v_block(uint16_t *slot, const uint16_t *blk,
+                                            size_t tok_stride, int n_valid) {
   constexpr int CPR = D / 8;
-  constexpr int SEG = kBlock * D * 2 / 1024;  // 1 KB segments
+  constexpr int SEG = kBlock * D * 2 / 1024;  // 1 KB per operation
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < SEG; ++i) {
     const int p = i * 64 + lane;
-    const int r = p / CPR, phys_c = p % CPR;
+    const int r = p / CPR, phys = p % CPR;
     const int swz = ((r & 3) << 1) | ((r >> 2) & 1);
-    const int tok = min(row_perm(r), n_valid - 1);
+    const int tok = min(r, n_valid - 1);
     __builtin_amdgcn_global_load_lds(
         (const __attribute__((address_space(1))) void *)(
-            blk + (size_t)tok * tok_stride + (phys_c ^ swz) * 8),
-        (__attribute__((address_space(3))) void *)(tile + i * 512), 16, 0, 0);
+            blk + (size_t)tok * tok_stride + (phys ^ swz) * 8),
+        (__attribute__((address_space(3))) void *)(slot + i * 512), 16, 0, 0);
   }
 }
 
 template <int D, int G, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
-  constexpr int TILE = kBlock * D;                 // bf16 per K or V tile
-  constexpr int SEG = kBlock * D * 2 / 1024;       // DMA ops per tile
-  constexpr int TCH = 256;                         // table entries per chunk
-  static_assert(G <= 32, "a query group must fit the 32 MFMA columns");
-  // Per wave: two buffers, each a K tile and a V tile.
-  __shared__ __attribute__((aligned(16))) uint16_t KVs[NW][2][2][TILE];
-  __shared__ int tab[TCH];
-  __shared__ float sm_m[NW][G], sm_l[NW][G];
-  __shared__ float sm_o[NW][G][D];
+  constexpr int TILE = kBlock * D;  // bf16 per V slot
+  constexpr int KS = D / 32;        // k-steps of S^T = K Q^T
+  constexpr int NC = D / 16;        // 16-row blocks of O^T
+  static_assert(G <= 16, "a query group must fit the 16 MFMA columns");
+  // One LDS object (the V slots, reused for the final merge), so that the
+  // compiler does not make LDS reads wait for DMA into other slots.
+  union Smem {
+    uint16_t v[NW][2][TILE];
+    struct {
+      float m[NW][G], l[NW][G];
+      float o[NW][G][D];
+    } red;
+  };
+  __shared__ __attribute__((aligned(16))) Smem sm;
 
   // KV heads vary fastest: the Hkv workgroups of one (split, sequence) are
-  // dispatched together and read the same cache blocks at once.
+  // dispatched together and read neighbouring tiles of the same blocks.
   const int hk = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ln = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;  // MFMA column / lane group
   const int S = a.num_splits;
   const int Hkv = a.Hkv;
 
@@ -77,145 +84,155 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   const int per = (nblk + S - 1) / S;
   const int t_begin = min(nblk, split * per);
   const int t_end = min(nblk, t_begin + per);
+  const int tw0 = t_begin + wave;  // this wave's blocks: tw0 + NW*j
+  const int cnt = tw0 < t_end ? (t_end - tw0 + NW - 1) / NW : 0;
 
-  // Scores are S^T = K Q^T on v_mfma_f32_32x32x16_bf16: MFMA rows are the
-  // block's 16 tokens (rows 16..31 are zero), columns the G query heads of
-  // this KV head's group (columns G..31 are zero).  Q as the B operand:
-  // lane = head column, slots = head dim.
-  bf16x8 qf[D / 16];
+  // Q as the B operand of S^T = K Q^T: column = head, k = head dim
+  // 32*ks + 8*grp + e.
+  bf16x8 qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (ln < G)
-      x = ldg128(a.q + ((size_t)b * a.Hq + hk * G + ln) * D + ks * 16 + 8 * hh);
+    if (col < G)
+      x = ldg128(a.q + ((size_t)b * a.Hq + hk * G + col) * D + ks * 32 + 8 * grp);
     qf[ks] = __builtin_bit_cast(bf16x8, x);
   }
 
-  // O^T accumulator: lane = head column, register r of cb holds head-dim row
-  // cb*32 + 8*(r/4) + 4*hh + (r%4).
-  f32x16 oacc[D / 32];
+  // O^T accumulator: lane = head column, register r of block cb holds
+  // head-dim row 16*cb + 4*grp + r.
+  f32x4 oacc[NC];
 #pragma unroll
-  for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[cb][r] = 0.f;
-  float m_run = kMaxInit, l_run = 0.f;  // raw score units; l over this half
+  for (int cb = 0; cb < NC; ++cb) oacc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kMaxInit, l_run = 0.f;  // raw score units; l over 4 tokens
   const float c = a.c;
 
   const int32_t *table = a.block_table + (size_t)b * a.max_blocks;
-  const size_t tok_stride = (size_t)Hkv * D;  // elements between tokens
-  const size_t head_off = (size_t)hk * D;
+  // Cache layout [num_blocks][Hkv][16][D]: one head's block tile is 16
+  // contiguous rows of D.
+  constexpr size_t tok_stride = D;
+  const size_t blk_stride = (size_t)Hkv * kBlock * D;
+  const size_t head_off = (size_t)hk * kBlock * D;
+  uint16_t(*slots)[TILE] = sm.v[wave];
 
-  for (int c0 = t_begin; c0 < t_end; c0 += TCH) {
-    const int c1 = min(t_end, c0 + TCH);
-    __syncthreads();  // previous chunk's table entries are no longer read
-    for (int x = tid; x < c1 - c0; x += 64 * NW) {
-      const int ph = table[c0 + x];
-      tab[x] = (ph >= 0 && ph < a.num_blocks) ? ph : -1;  // never read outside
+  // Transposing reads of V^T block cb: lane (grp, 4e + j) addresses token
+  // 4*grp + e, head-dim columns 16*cb + 4j .. +3 (slot 0; slot 1 is TILE
+  // elements further).
+  uint32_t va[NC];
+  {
+    const int e = col >> 2, j = col & 3;
+    const int r = 4 * grp + e;
+    const int swz = ((r & 3) << 1) | ((r >> 2) & 1);
+#pragma unroll
+    for (int cb = 0; cb < NC; ++cb) {
+      const int ch = 2 * cb + (j >> 1);
+      va[cb] = lds_addr(slots[0] + r * D + ((ch ^ swz) << 3) + 4 * (j & 1));
     }
-    __syncthreads();
-
-    // This wave's blocks: c0 + wave, +NW, ...; block i+1's DMA is issued
-    // before block i is computed (double buffer per wave).
-    auto issue = [&](int t, int buf) {
-      const int ph = tab[t - c0];
-      if (ph < 0) return;
-      const int n_valid = min(kBlock, len - t * kBlock);  // >= 1
-      const size_t boff = (size_t)ph * kBlock * tok_stride + head_off;
-      dma_block<D>(KVs[wave][buf][0], a.k_cache + boff, tok_stride, n_valid);
-      dma_block<D>(KVs[wave][buf][1], a.v_cache + boff, tok_stride, n_valid);
-    };
-    int buf = 0;
-    int t = c0 + wave;
-    if (t < c1) issue(t, 0);
-    for (; t < c1; t += NW, buf ^= 1) {
-      const bool has_next = t + NW < c1;
-      if (has_next) {
-        issue(t + NW, buf ^ 1);
-        // wait for this block's tiles; the next block's may stay in flight
-        if (tab[t + NW - c0] >= 0)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * SEG) : "memory");
-        else
-          wait_dma();
-      } else {
-        wait_dma();
-      }
-      if (tab[t - c0] < 0) continue;
-      const int n_valid = min(kBlock, len - t * kBlock);
-      const uint16_t *Kt = KVs[wave][buf][0];
-      const uint16_t *Vt = KVs[wave][buf][1];
-      f32x16 s;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        bf16x8 kf = {};
-        if (ln < kBlock) kf = lds_row_frag<D>(Kt, ln, ks * 16 + 8 * hh);
-        s = mfma32(kf, qf[ks], s);
-      }
-      // Registers 0..7 hold tokens 8*hh + r of this lane's head.
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const bool ok = 8 * hh + r < n_valid;
-        s[r] = ok ? s[r] : -INFINITY;
-        mx = fmaxf(mx, s[r]);
-      }
-      const float m_new = fmaxf(m_run, max_xor32(mx));
-      const float alpha = fast_exp2((m_run - m_new) * c);
-      const float mc = m_new * c;
-      m_run = m_new;
-      u32x4 pb;
-      float lsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p0 = fast_exp2(fmaf(s[2 * i], c, -mc));
-        const float p1 = fast_exp2(fmaf(s[2 * i + 1], c, -mc));
-        pb[i] = pack_bf16x2(p0, p1);
-        lsum = dot2_ones(pb[i], lsum);
-      }
-      l_run = fmaf(l_run, alpha, lsum);
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-        oacc[cb] = mfma32(lds_tr_frag<D>(Vt, 0, cb * 32),
-                          __builtin_bit_cast(bf16x8, pb), oacc[cb]);
-      }
-    }
-    wait_dma();
   }
 
-  // Merge the waves' states, then write the split's triple.
-  const float l_tot = sum_xor32(l_run);
-  if (ln < G) {
-    if (hh == 0) {
-      sm_m[wave][ln] = m_run;
-      sm_l[wave][ln] = l_tot;
+  for (int p0 = 0; p0 < cnt; p0 += 64) {
+    const int n = min(64, cnt - p0);
+    // Lane j holds the physical block of this pass's j-th block; entries
+    // outside [0, num_blocks) become -1: such a block is fetched from
+    // physical block 0 (always valid memory) and then skipped.
+    int ent = -1;
+    if (lane < n) {
+      const int ph = table[tw0 + NW * (p0 + lane)];
+      ent = (ph >= 0 && ph < a.num_blocks) ? ph : -1;
+    }
+    // K of block j: lane (grp, col) loads token col (clamped to the valid
+    // ones), head dims 32*ks + 8*grp .. +7; V of block j goes to slot j % 2.
+    auto fetch = [&](int j, bf16x8 (&kf)[KS]) {
+      const int ph = __builtin_amdgcn_readlane(ent, j);
+      const int t = tw0 + NW * (p0 + j);
+      const int n_valid = min(kBlock, len - t * kBlock);  // >= 1
+      const size_t boff = (size_t)max(ph, 0) * blk_stride + head_off;
+      const uint16_t *kb = a.k_cache + boff + (size_t)min(col, n_valid - 1) *
+                                                  tok_stride + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[ks] = __builtin_bit_cast(bf16x8, ldg128(kb + ks * 32));
+      dma_v_block<D>(slots[j & 1], a.v_cache + boff, tok_stride, n_valid);
+    };
+    bf16x8 kc[KS], kn[KS];
+    fetch(0, kc);
+    for (int j = 0; j < n; ++j) {
+      wait_dma();  // block j's K and V have landed; nothing else in flight
+      if (j + 1 < n) fetch(j + 1, kn);
+      const int ph = __builtin_amdgcn_readlane(ent, j);
+      if (ph >= 0) {
+        const int t = tw0 + NW * (p0 + j);
+        const int n_valid = min(kBlock, len - t * kBlock);
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s = mfma16k32(kc[ks], qf[ks], s);
+        // Register r holds token 4*grp + r of head col.
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[r] = 4 * grp + r < n_valid ? s[r] : -INFINITY;
+          mx = fmaxf(mx, s[r]);
+        }
+        const float m_new = fmaxf(m_run, max_xor32(max_xor16(mx)));
+        const float alpha = fast_exp2((m_run - m_new) * c);
+        const float mc = m_new * c;
+        m_run = m_new;
+        u32x2 pb;
+        pb[0] = pack_bf16x2(fast_exp2(fmaf(s[0], c, -mc)),
+                            fast_exp2(fmaf(s[1], c, -mc)));
+        pb[1] = pack_bf16x2(fast_exp2(fmaf(s[2], c, -mc)),
+                            fast_exp2(fmaf(s[3], c, -mc)));
+        l_run = fmaf(l_run, alpha, dot2_ones(pb[1], dot2_ones(pb[0], 0.f)));
+        uint32_t vaj[NC];
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb)
+          vaj[cb] = va[cb] + (uint32_t)((j & 1) * TILE * 2);
+        bf16x8 vf[NC / 2];  // two 16 x 16 V^T blocks per fragment
+        lds_tr_frags(vf, vaj);
+#pragma unroll
+        for (int cb = 0; cb < NC; ++cb) {
+          const u32x4 w = __builtin_bit_cast(u32x4, vf[cb >> 1]);
+          const u32x2 vb = (cb & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+          oacc[cb] = mfma16k16(vb, pb, oacc[cb] * alpha);
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kc[ks] = kn[ks];
+    }
+  }
+  wait_dma();
+
+  // Merge the waves' states, then write the split's triple.  The merge area
+  // overlays the V slots: every wave must be done with its slots first.
+  __syncthreads();
+  const float l_tot = sum_xor32(sum_xor16(l_run));
+  if (col < G) {
+    if (grp == 0) {
+      sm.red.m[wave][col] = m_run;
+      sm.red.l[wave][col] = l_tot;
     }
 #pragma unroll
-    for (int cb = 0; cb < D / 32; ++cb)
+    for (int cb = 0; cb < NC; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        sm_o[wave][ln][cb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3)] =
-            oacc[cb][r];
+      for (int r = 0; r < 4; ++r)
+        sm.red.o[wave][col][16 * cb + 4 * grp + r] = oacc[cb][r];
   }
   __syncthreads();
   const size_t pbase = ((size_t)b * a.Hq + hk * G) * S + split;
   for (int x = tid; x < G * D; x += 64 * NW) {
-    const int g = x / D, col = x % D;
-    float mx = sm_m[0][g];
+    const int g = x / D, dcol = x % D;
+    float mx = sm.red.m[0][g];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, sm_m[w][g]);
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, sm.red.m[w][g]);
     float acc = 0.f, lsum = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float wt = fast_exp2((sm_m[w][g] - mx) * c);
-      acc = fmaf(wt, sm_o[w][g][col], acc);
-      lsum = fmaf(wt, sm_l[w][g], lsum);
+      const float wt = fast_exp2((sm.red.m[w][g] - mx) * c);
+      acc = fmaf(wt, sm.red.o[w][g][dcol], acc);
+      lsum = fmaf(wt, sm.red.l[w][g], lsum);
     }
     const size_t pi = pbase + (size_t)g * S;
-    a.part_o[pi * D + col] = acc;
-    if (col == 0) {
+    a.part_o[pi * D + dcol] = acc;
+    if (dcol == 0) {
       a.part_m[pi] = mx;
       a.part_l[pi] = lsum;
     }
@@ -242,8 +259,8 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
 
 template <int D, int G>
 hipError_t decode_dispatch_g(const DecodeArgs &a, hipStream_t s) {
-  // Four waves per workgroup: two workgroups fit a CU's LDS at d = 128,
-  // and measured faster than one 8-wave workgroup.
+  // Four waves per workgroup (32.5 KB of LDS at d = 128: four workgroups
+  // per CU).
   constexpr int NW = 4;
   hipLaunchKernelGGL((decode_split_kernel<D, G, NW>),
                      dim3(a.Hkv, a.num_splits, a.B), dim3(64 * NW), 0, s, a);

@@ -83,6 +83,38 @@ __device__ __forceinline__ float sum_xor32(float x) {
          __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// x combined with the value of lane l ^ 16 (v_permlane16_swap exchanges the
+// odd 16-lane rows of its first operand with the even rows of its second).
+__device__ __forceinline__ float max_xor16(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]),
+               __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+__device__ __forceinline__ float sum_xor16(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) +
+         __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] B[32x16].  Lane l supplies
+// row (A) / column (B) l % 16 with k = 8*(l/16) + e; D: lane l holds column
+// l % 16, register r row 4*(l/16) + r.
+__device__ __forceinline__ f32x4 mfma16k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x16_bf16: as above with k = 4*(l/16) + e, e = 0..3 (each
+// operand is 4 bf16 packed in two dwords).
+__device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
+  typedef short shortx4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+      __builtin_bit_cast(shortx4, a), __builtin_bit_cast(shortx4, b), c, 0, 0,
+      0);
+}
+
 __device__ __forceinline__ u32x4 ldg128(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }
@@ -141,6 +173,79 @@ __device__ __forceinline__ bf16x8 lds_tr_frag(const uint16_t *tile, int kbase,
   typedef short shortx8 __attribute__((ext_vector_type(8)));
   const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// LDS byte addresses of the two 8-byte transposing reads (rows k and k + 4)
+// that make up lds_tr_frag<W>(tile, kbase, cbase) for the calling lane.
+template <int W>
+__device__ __forceinline__ void lds_tr_addr(const uint16_t *tile, int kbase,
+                                            int cbase, uint32_t &a0,
+                                            uint32_t &a1) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, t = lane & 15;
+  const int col = cbase + 16 * (g & 1) + 4 * (t & 3);
+  const int k0 = kbase + 8 * (g >> 1) + (t >> 2);
+  const int k1 = k0 + 4;
+  const int r0 = (k0 & ~31) | row_perm(k0 & 31);
+  const int r1 = (k1 & ~31) | row_perm(k1 & 31);
+  a0 = lds_addr(tile + lds_index(r0, col, W));
+  a1 = lds_addr(tile + lds_index(r1, col, W));
+}
+
+__device__ __forceinline__ bf16x8 tr_pair(u32x2 lo, u32x2 hi) {
+  const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Two / four transposed fragments (addresses from lds_tr_addr, in the order
+// a[2f], a[2f+1] for fragment f), read by one inline-asm statement that also
+// waits for them.  Unlike the compiler builtin, whose reads the compiler makes
+// wait for every outstanding direct-to-LDS DMA (vmcnt(0)), these leave DMA
+// into other buffers in flight.  The wait inside also drains any other LDS or
+// scalar-memory operation in flight, which is harmless.
+__device__ __forceinline__ void lds_tr_frags(bf16x8 (&f)[2],
+                                             const uint32_t (&a)[4]) {
+  u32x2 r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+  f[0] = tr_pair(r0, r1);
+  f[1] = tr_pair(r2, r3);
+}
+
+__device__ __forceinline__ void lds_tr_frags(bf16x8 (&f)[4],
+                                             const uint32_t (&a)[8]) {
+  u32x2 r0, r1, r2, r3, r4, r5, r6, r7;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5),
+        "=&v"(r6), "=&v"(r7)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]),
+        "v"(a[6]), "v"(a[7])
+      : "memory");
+  f[0] = tr_pair(r0, r1);
+  f[1] = tr_pair(r2, r3);
+  f[2] = tr_pair(r4, r5);
+  f[3] = tr_pair(r6, r7);
 }
 
 // 16-byte row fragment T[row][col .. col+7] from a swizzled tile (col % 8 == 0).

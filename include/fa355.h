@@ -144,9 +144,10 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
  *   d            head dimension, 64 or 128.
  *   q            [B,Hq,d] bf16.
  *   k_cache,
- *   v_cache      [num_blocks, block_size, Hkv, d] bf16.  Slots past a
- *                sequence's length are never read into the arithmetic (they
- *                may hold anything, NaN included).
+ *   v_cache      [num_blocks, Hkv, block_size, d] bf16 (head-major within a
+ *                block: one KV head's block_size x d tile is contiguous).
+ *                Slots past a sequence's length are never read into the
+ *                arithmetic (they may hold anything, NaN included).
  *   block_size   tokens per block; 16.
  *   block_table  device int32 [B, max_blocks_per_seq]; entries for t <
  *                ceil(seq_len/block_size) must be in [0, num_blocks).  An

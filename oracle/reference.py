@@ -169,7 +169,9 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None):
     the group's shared KV head.  Reading: query head hq uses KV head
     hq // (Hq / Hkv) (consecutive query heads share a KV head).
 
-    q: [B,Hq,d]; k_cache, v_cache: [num_blocks, block_size, Hkv, d];
+    q: [B,Hq,d]; k_cache, v_cache: [num_blocks, Hkv, block_size, d] (the
+    pages index one KV head's cache as cache[physical, :n]; with several
+    heads, each block keeps its heads one after another);
     block_table: int [B, max_blocks]; seq_lens: int [B].
     The plain definition is applied to the gathered keys: the method's loop is
     in ``online.paged_online``.  A sequence of length 0 gives out = 0.
@@ -177,8 +179,8 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None):
     """
     q = np.asarray(q, dtype=np.float64)
     B, Hq, d = q.shape
-    bs = k_cache.shape[1]
-    Hkv = k_cache.shape[2]
+    Hkv = k_cache.shape[1]
+    bs = k_cache.shape[2]
     G = Hq // Hkv
     sc = _default_scale(d, scale)
     out = np.zeros((B, Hq, v_cache.shape[3]))
@@ -191,14 +193,14 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None):
         for t in range(nblk):
             n = min(bs, L - t * bs)
             phys = int(block_table[b, t])
-            kk.append(np.asarray(k_cache[phys, :n], dtype=np.float64))
-            vv.append(np.asarray(v_cache[phys, :n], dtype=np.float64))
-        Kb = np.concatenate(kk, axis=0)  # [L, Hkv, d]
-        Vb = np.concatenate(vv, axis=0)
+            kk.append(np.asarray(k_cache[phys, :, :n], dtype=np.float64))
+            vv.append(np.asarray(v_cache[phys, :, :n], dtype=np.float64))
+        Kb = np.concatenate(kk, axis=1)  # [Hkv, L, d]
+        Vb = np.concatenate(vv, axis=1)
         for hq in range(Hq):
             hk = hq // G
-            s = sc * (Kb[:, hk, :] @ q[b, hq])
+            s = sc * (Kb[hk] @ q[b, hq])
             s = s - s.max()
             e = np.exp(s)
-            out[b, hq] = (e / e.sum()) @ Vb[:, hk, :]
+            out[b, hq] = (e / e.sum()) @ Vb[hk]
     return out

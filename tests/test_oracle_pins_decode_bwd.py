@@ -24,8 +24,8 @@ def _contiguous_to_paged(Kc, Vc, block_size, rng):
     total = sum(nblk)
     perm = rng.permutation(total)
     Hkv, d = Kc[0].shape[1:]
-    kc = np.full((total, block_size, Hkv, d), np.nan)
-    vc = np.full((total, block_size, Hkv, d), np.nan)
+    kc = np.full((total, Hkv, block_size, d), np.nan)
+    vc = np.full((total, Hkv, block_size, d), np.nan)
     table = np.full((len(lens), max(nblk)), -1)
     off = 0
     for b, L in enumerate(lens):
@@ -33,8 +33,9 @@ def _contiguous_to_paged(Kc, Vc, block_size, rng):
             phys = perm[off + t]
             table[b, t] = phys
             n = min(block_size, L - t * block_size)
-            kc[phys, :n] = Kc[b][t * block_size:t * block_size + n]
-            vc[phys, :n] = Vc[b][t * block_size:t * block_size + n]
+            rows = slice(t * block_size, t * block_size + n)
+            kc[phys, :, :n] = Kc[b][rows].transpose(1, 0, 2)
+            vc[phys, :, :n] = Vc[b][rows].transpose(1, 0, 2)
         off += nblk[b]
     return kc, vc, table
 
@@ -89,8 +90,8 @@ def test_paged_online_loop_equals_paged_definition():
                        cache.block_table, lens)
     for b in range(4):
         o = paged_online(q[b, 0], cache.block_table[b],
-                         cache.k_cache.exact[:, :, 0],
-                         cache.v_cache.exact[:, :, 0], int(lens[b]), 16)
+                         cache.k_cache.exact[:, 0],
+                         cache.v_cache.exact[:, 0], int(lens[b]), 16)
         assert np.max(np.abs(o - ref[b, 0])) <= 1e-13
 
 

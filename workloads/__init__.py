@@ -83,7 +83,7 @@ def uniform_int(n, lo, hi, cfg_seed, tensor_id):
 
 @dataclass
 class Paged:
-    """A paged KV cache: [num_blocks, block_size, Hkv, d] plus block table."""
+    """A paged KV cache: [num_blocks, Hkv, block_size, d] plus block table."""
     k_cache: Tensor
     v_cache: Tensor
     block_table: np.ndarray   # int32 [B, max_blocks], -1 where unused
@@ -107,7 +107,7 @@ def paged_cache(seq_lens, Hkv, d, block_size, max_blocks, cfg_seed,
     for b in range(B):
         table[b, :nblk[b]] = perm[off:off + nblk[b]]
         off += nblk[b]
-    shape = (total, block_size, Hkv, d)
+    shape = (total, Hkv, block_size, d)
     kc = rng(cfg_seed, TID_KC).standard_normal(size=shape, dtype=np.float32)
     vc = rng(cfg_seed, TID_VC).standard_normal(size=shape, dtype=np.float32)
     if poison_tails:
@@ -115,8 +115,8 @@ def paged_cache(seq_lens, Hkv, d, block_size, max_blocks, cfg_seed,
             L = int(seq_lens[b])
             if nblk[b] and L % block_size:
                 last = table[b, nblk[b] - 1]
-                kc[last, L % block_size:] = np.nan
-                vc[last, L % block_size:] = np.nan
+                kc[last, :, L % block_size:] = np.nan
+                vc[last, :, L % block_size:] = np.nan
     kb, vb = bf16_bits(kc), bf16_bits(vc)
     return Paged(Tensor("bf16", kb, bf16_value(kb).astype(np.float64)),
                  Tensor("bf16", vb, bf16_value(vb).astype(np.float64)),
