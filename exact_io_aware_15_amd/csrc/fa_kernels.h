@@ -37,7 +37,7 @@ hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, hipStream_t s);
 
 struct DecodeArgs {
   const uint16_t *q;            // [B,Hq,d]
-  const uint16_t *k_cache;      // [num_blocks, block_size, Hkv, d]
+  const uint16_t *k_cache;      // [num_blocks, Hkv, block_size, d]
   const uint16_t *v_cache;
   const int32_t *block_table;   // [B, max_blocks]
   const int32_t *seq_lens;      // [B]
