@@ -27,6 +27,8 @@
 // score registers come out as 8 consecutive rows per lane (see fa_device.h);
 // operands that contract over a tile's rows are read with transposing LDS
 // loads (lds_tr_frag) instead of being stored transposed.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -74,7 +76,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(16))) float LDs[2][2 * BR];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform: readfirstlane lets the compiler see it, so
+  // per-wave conditions (diagonal tiles) become scalar branches.
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hh = lane >> 5;
   const int N = a.N;
   const int bh = blockIdx.x % a.BH;
@@ -178,31 +182,38 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         dp = mfma32(df, vb[ks], dp);
       }
       // Register r holds query qs + 16*(r/8) + 8*hh + (r%8) of this key.
+      // The mask test is wave-uniform: a scalar branch picks the variant.
       const bool need_mask =
           (kw + 32 > kv_valid) || (CAUSAL && qs < kw + 31);
       uint32_t pp[8], ps[8];
+      auto probs = [&](auto masked_tile) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // registers 2i, 2i+1 hold two consecutive queries: one 16-byte read
-        // gives both (lse2, D) pairs
-        const int qo0 = 32 * qb + 16 * (i >> 2) + 8 * hh + 2 * (i & 3);
-        const f32x4 st = *reinterpret_cast<const f32x4 *>(&LDt[2 * qo0]);
-        float pv[2], dsv[2];
+        for (int i = 0; i < 8; ++i) {
+          // registers 2i, 2i+1 hold two consecutive queries: one 16-byte
+          // read gives both (lse2, D) pairs
+          const int qo0 = 32 * qb + 16 * (i >> 2) + 8 * hh + 2 * (i & 3);
+          const f32x4 st = *reinterpret_cast<const f32x4 *>(&LDt[2 * qo0]);
+          float pv[2], dsv[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int r = 2 * i + t;
-          float p = fast_exp2(fmaf(s[r], c, -st[2 * t]));
-          if (need_mask) {
-            const bool masked =
-                key >= kv_valid || (CAUSAL && key > q0 + qo0 + t);
-            p = masked ? 0.f : p;
+          for (int t = 0; t < 2; ++t) {
+            const int r = 2 * i + t;
+            float p = fast_exp2(fmaf(s[r], c, -st[2 * t]));
+            if (decltype(masked_tile)::value) {
+              const bool masked =
+                  key >= kv_valid || (CAUSAL && key > q0 + qo0 + t);
+              p = masked ? 0.f : p;
+            }
+            pv[t] = p;
+            dsv[t] = p * (dp[r] - st[2 * t + 1]);
           }
-          pv[t] = p;
-          dsv[t] = p * (dp[r] - st[2 * t + 1]);
+          pp[i] = pack_bf16x2(pv[0], pv[1]);
+          ps[i] = pack_bf16x2(dsv[0], dsv[1]);
         }
-        pp[i] = pack_bf16x2(pv[0], pv[1]);
-        ps[i] = pack_bf16x2(dsv[0], dsv[1]);
-      }
+      };
+      if (need_mask)
+        probs(std::true_type{});
+      else
+        probs(std::false_type{});
       // dV += P^T dO, dK += dS^T Q: A = this lane's registers (lane = key,
       // slots = 8 consecutive queries), B = transposed Q / dO fragments.
 #pragma unroll
@@ -253,7 +264,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hh = lane >> 5;
   const int N = a.N;
   const int nqt = (N + BR - 1) / BR;
@@ -329,25 +340,33 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
           s = mfma32(kf, qf[ks], s);
           dp = mfma32(vf, df[ks], dp);
         }
-        // Register r holds key k0 + 32*kb + 16*(r/8) + 8*hh + (r%8).
+        // Register r holds key k0 + 32*kb + 16*(r/8) + 8*hh + (r%8).  The
+        // mask test is wave-uniform: a scalar branch picks the variant.
         const bool need_mask =
             (k0 + BC > kv_valid) || (CAUSAL && k0 + BC - 1 > qw);
+        auto grads = [&](auto masked_tile) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float dsv[2];
+          for (int i = 0; i < 8; ++i) {
+            float dsv[2];
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int r = 2 * i + u;
-            float p = fast_exp2(fmaf(s[r], c, -lrow));
-            if (need_mask) {
-              const int kk = k0 + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
-              const bool masked = kk >= kv_valid || (CAUSAL && kk > qi);
-              p = masked ? 0.f : p;
+            for (int u = 0; u < 2; ++u) {
+              const int r = 2 * i + u;
+              float p = fast_exp2(fmaf(s[r], c, -lrow));
+              if (decltype(masked_tile)::value) {
+                const int kk =
+                    k0 + 32 * kb + 16 * (r >> 3) + 8 * hh + (r & 7);
+                const bool masked = kk >= kv_valid || (CAUSAL && kk > qi);
+                p = masked ? 0.f : p;
+              }
+              dsv[u] = p * (dp[r] - drow);
             }
-            dsv[u] = p * (dp[r] - drow);
+            ps[kb][i] = pack_bf16x2(dsv[0], dsv[1]);
           }
-          ps[kb][i] = pack_bf16x2(dsv[0], dsv[1]);
-        }
+        };
+        if (need_mask)
+          grads(std::true_type{});
+        else
+          grads(std::false_type{});
       }
       // dQ^T += K^T dS^T: A = transposed K fragments, B = this lane's dS^T.
 #pragma unroll
