@@ -29,9 +29,20 @@ namespace {
 
 constexpr int kBlock = 16;  // tokens per cache block
 
+// Chunk permutation of a 16-row V tile (row r, bits r0..r2): the 16 x 16
+// transposing reads (4 rows x 2 adjacent chunks per 16 lanes) are free of
+// bank conflicts whether the LDS serves 128 or 256 bytes per cycle.
+//   D = 64:  (r0^r2) << 1 | r1 << 2
+//   D = 128: r0 << 1 | r1 << 2 | r2 << 3
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {
+  if (D == 64) return (((r ^ (r >> 2)) & 1) << 1) | (((r >> 1) & 1) << 2);
+  return ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 3);
+}
+
 // Issues the DMA of one block's V tile (16 tokens x D of one KV head) into
 // an LDS slot: row r holds token r, its 16-byte chunk c at position
-// c ^ swz(r).  Slots past the sequence read its last valid token instead
+// c ^ v_swz(r).  Slots past the sequence read its last valid token instead
 // (finite data that gets probability 0).
 template <int D>
 __device__ __forceinline__ void dma_v_block(uint16_t *slot, const uint16_t *blk,
@@ -43,11 +54,10 @@ __device__ __forceinline__ void dma_v_block(uint16_t *slot, const uint16_t *blk,
   for (int i = 0; i < SEG; ++i) {
     const int p = i * 64 + lane;
     const int r = p / CPR, phys = p % CPR;
-    const int swz = ((r & 3) << 1) | ((r >> 2) & 1);
     const int tok = min(r, n_valid - 1);
     __builtin_amdgcn_global_load_lds(
         (const __attribute__((address_space(1))) void *)(
-            blk + (size_t)tok * tok_stride + (phys ^ swz) * 8),
+            blk + (size_t)tok * tok_stride + (phys ^ v_swz<D>(r)) * 8),
         (__attribute__((address_space(3))) void *)(slot + i * 512), 16, 0, 0);
   }
 }
@@ -121,7 +131,7 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   {
     const int e = col >> 2, j = col & 3;
     const int r = 4 * grp + e;
-    const int swz = ((r & 3) << 1) | ((r >> 2) & 1);
+    const int swz = v_swz<D>(r);
 #pragma unroll
     for (int cb = 0; cb < NC; ++cb) {
       const int ch = 2 * cb + (j >> 1);

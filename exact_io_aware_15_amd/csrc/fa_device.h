@@ -130,17 +130,28 @@ __device__ __forceinline__ int row_perm(int p) {
   return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
 }
 
-// LDS operand tiles hold rows of D bf16 with no padding; the 16-byte chunks
-// of row r are stored XOR-permuted by swz(r) = 2*(r%4) + (r/4)%2.  Eight
-// consecutive rows then put one logical chunk in eight different chunk slots
-// (a 16-byte read pass of 8 lanes touches all 32 banks once), and four
-// consecutive rows put a pair of adjacent logical chunks in four disjoint
-// slot pairs (an 8-byte transposing read pass of 16 lanes, see lds_tr_frag,
-// is conflict-free too).  Every access computes its slot from the logical
-// (row, column), so the permutation is invisible to the arithmetic.
-__device__ __forceinline__ int lds_index(int row, int col, int width) {
-  const int swz = ((row & 3) << 1) | ((row >> 2) & 1);
-  return row * width + ((((col >> 3) ^ swz)) << 3) + (col & 7);
+// LDS operand tiles hold rows of W bf16 with no padding; the 16-byte chunks
+// of row r are stored XOR-permuted by lds_swz<W>(r) (r0..r3 = bits of r):
+//   W = 64  (8 chunks):  r2 | (r0^r3) << 1 | r1 << 2
+//   W = 128 (16 chunks): r2 | r1 << 1 | r0 << 2 | (r1^r3) << 3
+// Either way both kinds of operand read are free of bank conflicts whether
+// the LDS serves 128 or 256 bytes per cycle: a 16-byte row-fragment read
+// (one chunk of 8 or 16 consecutive rows per pass) and an 8-byte transposing
+// read (4 consecutive rows x 2 or 4 adjacent chunks per pass, lds_tr_frag).
+// Every access computes its slot from the logical (row, column), so the
+// permutation is invisible to the arithmetic.
+template <int W>
+__device__ __forceinline__ int lds_swz(int r) {
+  static_assert(W == 64 || W == 128, "tile width");
+  if (W == 64)
+    return ((r >> 2) & 1) | (((r ^ (r >> 3)) & 1) << 1) | (((r >> 1) & 1) << 2);
+  return ((r >> 2) & 1) | (((r >> 1) & 1) << 1) | ((r & 1) << 2) |
+         ((((r >> 1) ^ (r >> 3)) & 1) << 3);
+}
+
+template <int W>
+__device__ __forceinline__ int lds_index(int row, int col) {
+  return row * W + (((col >> 3) ^ lds_swz<W>(row)) << 3) + (col & 7);
 }
 
 // Transposed MFMA fragment from a swizzled bf16 tile in LDS (row width W),
@@ -166,10 +177,10 @@ __device__ __forceinline__ bf16x8 lds_tr_frag(const uint16_t *tile, int kbase,
   const int r1 = (k1 & ~31) | row_perm(k1 & 31);
   const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) shortx4 *)(tile +
-                                                    lds_index(r0, col, W)));
+                                                    lds_index<W>(r0, col)));
   const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) shortx4 *)(tile +
-                                                    lds_index(r1, col, W)));
+                                                    lds_index<W>(r1, col)));
   typedef short shortx8 __attribute__((ext_vector_type(8)));
   const shortx8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
@@ -193,8 +204,8 @@ __device__ __forceinline__ void lds_tr_addr(const uint16_t *tile, int kbase,
   const int k1 = k0 + 4;
   const int r0 = (k0 & ~31) | row_perm(k0 & 31);
   const int r1 = (k1 & ~31) | row_perm(k1 & 31);
-  a0 = lds_addr(tile + lds_index(r0, col, W));
-  a1 = lds_addr(tile + lds_index(r1, col, W));
+  a0 = lds_addr(tile + lds_index<W>(r0, col));
+  a1 = lds_addr(tile + lds_index<W>(r1, col));
 }
 
 __device__ __forceinline__ bf16x8 tr_pair(u32x2 lo, u32x2 hi) {
@@ -253,14 +264,14 @@ template <int W>
 __device__ __forceinline__ bf16x8 lds_row_frag(const uint16_t *tile, int row,
                                                int col) {
   return __builtin_bit_cast(
-      bf16x8, *reinterpret_cast<const u32x4 *>(tile + lds_index(row, col, W)));
+      bf16x8, *reinterpret_cast<const u32x4 *>(tile + lds_index<W>(row, col)));
 }
 
 // Stores a 16-byte chunk of logical row `row` (any row order) at column col.
 template <int W>
 __device__ __forceinline__ void lds_store_chunk(uint16_t *tile, int row,
                                                 int col, u32x4 x) {
-  *reinterpret_cast<u32x4 *>(tile + lds_index(row, col, W)) = x;
+  *reinterpret_cast<u32x4 *>(tile + lds_index<W>(row, col)) = x;
 }
 
 // Fills an LDS operand tile of ROWS x W bf16 (swizzled, rows in row_perm
@@ -282,9 +293,8 @@ __device__ __forceinline__ void dma_tile(uint16_t *tile, const uint16_t *src,
     const int seg = wave + 4 * u;
     const int p = seg * 64 + lane;          // 16-byte slot in the tile
     const int r = p / CPR, phys = p % CPR;  // storage row, chunk slot
-    const int swz = ((r & 3) << 1) | ((r >> 2) & 1);
     const int row = min(row0 + ((r & ~31) | row_perm(r & 31)), last_row);
-    const size_t goff = (size_t)row * W + (phys ^ swz) * 8;
+    const size_t goff = (size_t)row * W + (phys ^ lds_swz<W>(r)) * 8;
     __builtin_amdgcn_global_load_lds(
         (const __attribute__((address_space(1))) void *)(src + goff),
         (__attribute__((address_space(3))) void *)(tile + seg * 512), 16, 0,
