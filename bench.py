@@ -92,6 +92,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt2_medium_causal_4k")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the paged decode (paged_gqa_decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -183,10 +185,17 @@ def decode_bench(steps, warmup, splits=None):
     total_len = int(np.sum(cache.seq_lens))
     # K and V rows read: len * Hkv * d * 2 bytes each
     kv_bytes = total_len * w.Hkv * w.d * 2 * 2
+    gbs = kv_bytes / ms / 1e6
     return {"workload": w.name, "num_splits": splits, "ms": round(ms, 4),
             "kv_bytes": kv_bytes,
-            "GB/s": round(kv_bytes / ms / 1e6, 1),
-            "frac_of_hbm_peak": round(kv_bytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+            "GB/s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "roofline": {"kernel": "fa_decode_paged (decode_split_kernel + "
+                                   "decode_merge_kernel launches)",
+                         "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": traffic_for("fa_decode_paged")}}
 
 
 def sweep(steps, warmup):
@@ -280,6 +289,9 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": args.copy_bytes, "steps": args.steps}))
+        return
+    if args.decode_only:
+        print(json.dumps(decode_bench(args.steps, args.warmup)), flush=True)
         return
     w = WORKLOADS[args.workload]
     attn = Attn(w)
