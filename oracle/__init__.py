@@ -27,6 +27,8 @@ Modules:
   tiled forward of FA notes §3.2, the S12 deferred-normalisation recurrence,
   the split-K (m, l, o) merge of S12 exercise 1, and the S12 paged loop.
 * ``brute``     -- pure-Python scalar loops for tiny inputs.
+* ``varlen``    -- packed variable-length batches (block-diagonal visibility),
+  forward and backward.
 
 Pin status: every public function here is pinned by the CPU tests against
 closed forms, invariants, brute force or finite differences; none is marked
@@ -48,3 +50,8 @@ from .online import (  # noqa: F401
     paged_online,
 )
 from .brute import brute_fwd  # noqa: F401
+from .varlen import (  # noqa: F401
+    attention_bwd_varlen,
+    attention_fwd_varlen,
+    varlen_visible,
+)
