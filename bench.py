@@ -111,19 +111,35 @@ class Attn:
         import exact_io_aware_15_amd as fa
         from workloads import to_device
         self.w, self.fa, self.torch = w, fa, torch
-        q, k, v = w.qkv()
+        self.varlen = w.kind == "varlen"
+        if self.varlen:   # packed ragged batch, [H, total, d]
+            cu, q, k, v = w.varlen_inputs()
+            self.cu = torch.from_numpy(cu).cuda()
+            self.do = to_device(w.varlen_dout())
+            nbytes = fa.bwd_varlen_workspace_bytes(w.H, int(cu[-1]), w.d)
+            self.kv_len = None
+        else:
+            q, k, v = w.qkv()
+            self.do = to_device(w.dout())
+            kl = w.kv_len()
+            self.kv_len = None if kl is None else torch.from_numpy(kl).cuda()
+            nbytes = fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d)
         self.q, self.k, self.v = (to_device(t) for t in (q, k, v))
-        self.do = to_device(w.dout())
-        kl = w.kv_len()
-        self.kv_len = None if kl is None else torch.from_numpy(kl).cuda()
-        self.ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d),
-                              dtype=torch.uint8, device="cuda")
+        self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8,
+                              device="cuda")
 
     def fwd(self):
+        if self.varlen:
+            return self.fa.fwd_varlen(self.q, self.k, self.v, self.cu,
+                                      self.w.N, causal=self.w.causal)
         return self.fa.fwd(self.q, self.k, self.v, causal=self.w.causal,
                            kv_len=self.kv_len)
 
     def bwd(self, o, m, l):
+        if self.varlen:
+            return self.fa.bwd_varlen(self.q, self.k, self.v, o, self.do, m,
+                                      l, self.cu, self.w.N,
+                                      causal=self.w.causal, workspace=self.ws)
         return self.fa.bwd(self.q, self.k, self.v, o, self.do, m, l,
                            causal=self.w.causal, kv_len=self.kv_len,
                            workspace=self.ws)
@@ -202,7 +218,8 @@ def sweep(steps, warmup):
     from workloads import WORKLOADS
     out = {}
     for name in ["bert_large_padded", "gpt2_medium_causal_1k",
-                 "long_causal_16k_d128", "long_causal_64k_d64"]:
+                 "long_causal_16k_d128", "long_causal_64k_d64",
+                 "varlen_causal_prefill"]:
         w = WORKLOADS[name]
         attn = Attn(w)
         step_ms, fwd_ms, bwd_ms, _ = time_step(attn, steps, warmup,

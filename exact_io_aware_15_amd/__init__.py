@@ -8,6 +8,8 @@ the library is missing, the calls raise.
 
     o, m, l = fwd(q, k, v, causal=False, kv_len=None, scale=None)
     dq, dk, dv = bwd(q, k, v, o, do, m, l, causal=False, kv_len=None)
+    o, m, l = fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False)
+    dq, dk, dv = bwd_varlen(q, k, v, o, do, m, l, cu_seqlens, max_seqlen)
     out = decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits=8)
 """
 
@@ -15,7 +17,8 @@ import math
 
 from ._lib import FA_BF16, FA_F32, FaError, LibraryMissing, check, lib
 
-__all__ = ["fwd", "bwd", "decode_paged", "bwd_workspace_bytes",
+__all__ = ["fwd", "bwd", "fwd_varlen", "bwd_varlen", "decode_paged",
+           "bwd_workspace_bytes", "bwd_varlen_workspace_bytes",
            "decode_workspace_bytes", "FaError", "LibraryMissing"]
 
 
@@ -115,6 +118,74 @@ def bwd(q, k, v, o, do, m, l, causal=False, kv_len=None, scale=None,
                           _ptr(dv), _ptr(workspace), workspace.numel(),
                           _stream(q))
     check("fa_bwd", st)
+    return dq, dk, dv
+
+
+def _cu_seqlens(cu, device):
+    torch = _torch()
+    if not torch.is_tensor(cu):
+        cu = torch.tensor(list(cu), dtype=torch.int32, device=device)
+    _check_dev("cu_seqlens", cu, torch.int32)
+    if cu.dim() != 1 or cu.numel() < 2:
+        raise ValueError("cu_seqlens must be [B+1] with B >= 1")
+    return cu
+
+
+def fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, scale=None,
+               return_stats=True):
+    """Exact attention on a packed ragged batch.  q, k, v: [H,total,d] bf16 or
+    fp32 (head-major packed); sequence b is tokens cu_seqlens[b] ..
+    cu_seqlens[b+1]-1 and attends only itself.  max_seqlen: at least every
+    sequence's length.  Returns (o, m, l) with m, l fp32 [H,total]."""
+    torch = _torch()
+    H, total, d = q.shape
+    _check_dev("q", q)
+    _check_dev("k", k, q.dtype, q.shape)
+    _check_dev("v", v, q.dtype, q.shape)
+    cu = _cu_seqlens(cu_seqlens, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    m = l = None
+    if return_stats:
+        m = torch.empty((H, total), dtype=torch.float32, device=q.device)
+        l = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib().fa_fwd_varlen(_dtype_code(q), cu.numel() - 1, H, total,
+                                 int(max_seqlen), d, _ptr(cu), _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(o), _ptr(m), _ptr(l),
+                                 int(bool(causal)), scale, _stream(q))
+    check("fa_fwd_varlen", st)
+    return o, m, l
+
+
+def bwd_varlen_workspace_bytes(H, total, d):
+    return int(lib().fa_bwd_varlen_workspace_bytes(H, total, d))
+
+
+def bwd_varlen(q, k, v, o, do, m, l, cu_seqlens, max_seqlen, causal=False,
+               scale=None, workspace=None):
+    """Gradients (dq, dk, dv) for fwd_varlen; bf16 [H,total,d]."""
+    torch = _torch()
+    H, total, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_dev(name, t, torch.bfloat16, (H, total, d))
+    _check_dev("m", m, torch.float32, (H, total))
+    _check_dev("l", l, torch.float32, (H, total))
+    cu = _cu_seqlens(cu_seqlens, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = bwd_varlen_workspace_bytes(H, total, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8,
+                                device=q.device)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    with torch.cuda.device(q.device):
+        st = lib().fa_bwd_varlen(cu.numel() - 1, H, total, int(max_seqlen), d,
+                                 _ptr(cu), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                 _ptr(do), _ptr(m), _ptr(l),
+                                 int(bool(causal)), scale, _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(workspace), workspace.numel(),
+                                 _stream(q))
+    check("fa_bwd_varlen", st)
     return dq, dk, dv
 
 

@@ -27,6 +27,16 @@ bool attn_shape_ok(int B, int H, int N) {
 // The HIP error behind the calling thread's most recent FA_E_HIP.
 thread_local hipError_t last_hip_error = hipSuccess;
 
+// Packed variable-length problems: B sequences of at most max_seqlen tokens
+// in [H, total, d] matrices.  The grids span ceil(max_seqlen / 64) tiles per
+// (sequence, head).
+bool varlen_shape_ok(int B, int H, int total, int max_seqlen) {
+  if (B < 1 || H < 1 || total < 0 || max_seqlen < 1 || max_seqlen > kMaxN)
+    return false;
+  if ((long long)H * total > (1LL << 31) - 1) return false;
+  return (long long)((max_seqlen + 63) / 64) * B * H <= (1LL << 31) - 1;
+}
+
 int from_hip(hipError_t e) {
   if (e == hipSuccess) return FA_OK;
   last_hip_error = e;
@@ -65,6 +75,7 @@ int fa_fwd(int dtype, int B, int H, int N, int d, const void *q,
   if (dtype != FA_BF16 && dtype != FA_F32) return FA_E_UNSUPPORTED;
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o; a.m = m; a.l = l; a.kv_len = kv_len;
+  a.cu_seqlens = nullptr; a.total = 0;
   a.B = B; a.H = H; a.N = N; a.BH = B * H;
   a.scale = scale;
   a.c = (float)((double)scale * 1.4426950408889634);
@@ -96,11 +107,73 @@ int fa_bwd(int B, int H, int N, int d, const void *q, const void *k,
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k;
   a.v = (const uint16_t *)v; a.o = (const uint16_t *)o;
   a.dout = (const uint16_t *)dout; a.m = m; a.l = l; a.kv_len = kv_len;
+  a.cu_seqlens = nullptr; a.total = 0; a.rows = (long long)rows;
   a.dq = (uint16_t *)dq; a.dk = (uint16_t *)dk; a.dv = (uint16_t *)dv;
   char *ws = (char *)workspace;
   a.lse2 = (float *)ws;
   a.delta = (float *)(ws + align_up(rows * sizeof(float)));
   a.B = B; a.H = H; a.N = N; a.BH = B * H;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  return from_hip(launch_bwd(a, d, causal != 0, (hipStream_t)stream));
+}
+
+int fa_fwd_varlen(int dtype, int B, int H, int total, int max_seqlen, int d,
+                  const int32_t *cu_seqlens, const void *q, const void *k,
+                  const void *v, void *o, float *m, float *l, int causal,
+                  float scale, void *stream) {
+  if (!varlen_shape_ok(B, H, total, max_seqlen) || !valid_scale(scale))
+    return FA_E_SHAPE;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_F32) return FA_E_UNSUPPORTED;
+  if (total == 0) return FA_OK;  // no rows (empty buffers may be NULL)
+  if (!cu_seqlens || !q || !k || !v || !o) return FA_E_NULLPTR;
+  if ((m == nullptr) != (l == nullptr)) return FA_E_NULLPTR;
+  FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.m = m; a.l = l; a.kv_len = nullptr;
+  a.cu_seqlens = cu_seqlens; a.total = total;
+  a.B = B; a.H = H; a.N = max_seqlen; a.BH = B * H;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == FA_BF16) return from_hip(launch_fwd_bf16(a, d, causal != 0, s));
+  return from_hip(launch_fwd_f32(a, d, causal != 0, s));
+}
+
+size_t fa_bwd_varlen_workspace_bytes(int H, int total, int d) {
+  if (H < 1 || total < 0 || (long long)H * total > (1LL << 31) - 1 ||
+      (d != 64 && d != 128))
+    return 0;
+  return 2 * align_up((size_t)H * total * sizeof(float));
+}
+
+int fa_bwd_varlen(int B, int H, int total, int max_seqlen, int d,
+                  const int32_t *cu_seqlens, const void *q, const void *k,
+                  const void *v, const void *o, const void *dout,
+                  const float *m, const float *l, int causal, float scale,
+                  void *dq, void *dk, void *dv, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+  if (!varlen_shape_ok(B, H, total, max_seqlen) || !valid_scale(scale))
+    return FA_E_SHAPE;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  if (total == 0) return FA_OK;  // no rows (empty buffers may be NULL)
+  if (!cu_seqlens || !q || !k || !v || !o || !dout || !m || !l || !dq ||
+      !dk || !dv)
+    return FA_E_NULLPTR;
+  const size_t need = fa_bwd_varlen_workspace_bytes(H, total, d);
+  if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
+  if (((uintptr_t)workspace) % kAlign) return FA_E_WORKSPACE;
+  const size_t rows = (size_t)H * total;
+  BwdArgs a;
+  a.q = (const uint16_t *)q; a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v; a.o = (const uint16_t *)o;
+  a.dout = (const uint16_t *)dout; a.m = m; a.l = l; a.kv_len = nullptr;
+  a.cu_seqlens = cu_seqlens; a.total = total; a.rows = (long long)rows;
+  a.dq = (uint16_t *)dq; a.dk = (uint16_t *)dk; a.dv = (uint16_t *)dv;
+  char *ws = (char *)workspace;
+  a.lse2 = (float *)ws;
+  a.delta = (float *)(ws + align_up(rows * sizeof(float)));
+  a.B = B; a.H = H; a.N = max_seqlen; a.BH = B * H;
   a.scale = scale;
   a.c = (float)((double)scale * 1.4426950408889634);
   return from_hip(launch_bwd(a, d, causal != 0, (hipStream_t)stream));

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   constexpr int CPR = D / 8;
   constexpr int RPB = 256 / CPR;  // rows per block
   const int tid = threadIdx.x;
-  const long long total = (long long)a.BH * a.N;
+  const long long total = a.rows;
   const long long r = (long long)blockIdx.x * RPB + tid / CPR;
   const int cc = tid % CPR;
   float part = 0.f;
@@ -80,11 +80,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   // per-wave conditions (diagonal tiles) become scalar branches.
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hh = lane >> 5;
-  const int N = a.N;
   const int bh = blockIdx.x % a.BH;
   const int kt = blockIdx.x / a.BH;  // causal: low key tiles carry most work
   const int b = bh / a.H;
-  const size_t hoff = (size_t)bh * N * D;
+  const SliceRows sr = slice_rows(a.cu_seqlens, a.total, a.N, a.H, bh);
+  const int N = sr.n;
+  const size_t hoff = sr.row0 * D;
   const int j0 = kt * BC;
   const int kw = j0 + 32 * wave;
   const int key = kw + ln;
@@ -110,8 +111,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   const uint16_t *kg = a.k + hoff;
   const uint16_t *vg = a.v + hoff;
   const uint16_t *dog = a.dout + hoff;
-  const float *lse2 = a.lse2 + (size_t)bh * N;
-  const float *dlt = a.delta + (size_t)bh * N;
+  const float *lse2 = a.lse2 + sr.row0;
+  const float *dlt = a.delta + sr.row0;
 
   // This wave's 32 keys as B operands (lane = key, slots = head dim).
   bf16x8 kb[D / 16], vb[D / 16];
@@ -266,13 +267,15 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hh = lane >> 5;
-  const int N = a.N;
-  const int nqt = (N + BR - 1) / BR;
+  const int nqt = (a.N + BR - 1) / BR;
   const int bh = blockIdx.x % a.BH;
   const int qt = nqt - 1 - (int)(blockIdx.x / a.BH);  // heaviest first
   const int b = bh / a.H;
-  const size_t hoff = (size_t)bh * N * D;
+  const SliceRows sr = slice_rows(a.cu_seqlens, a.total, a.N, a.H, bh);
+  const int N = sr.n;
+  const size_t hoff = sr.row0 * D;
   const int q0 = qt * BR;
+  if (q0 >= N) return;  // a packed sequence shorter than the longest one
   const int qw = q0 + 32 * wave;
   const int qi = qw + ln;
   int kv_valid = N;
@@ -299,8 +302,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
     qf[ks] = __builtin_bit_cast(bf16x8, x);
     df[ks] = __builtin_bit_cast(bf16x8, y);
   }
-  const float lrow = qi < N ? a.lse2[(size_t)bh * N + qi] : INFINITY;
-  const float drow = qi < N ? a.delta[(size_t)bh * N + qi] : 0.f;
+  const float lrow = qi < N ? a.lse2[sr.row0 + qi] : INFINITY;
+  const float drow = qi < N ? a.delta[sr.row0 + qi] : 0.f;
 
   f32x16 dq[D / 32];
 #pragma unroll
@@ -414,7 +417,7 @@ void bwd_launch_main(const BwdArgs &a, hipStream_t st) {
 
 template <int D, bool CAUSAL>
 hipError_t bwd_dispatch(const BwdArgs &a, hipStream_t st) {
-  const long long rows = (long long)a.BH * a.N;
+  const long long rows = a.rows;
   const int rpb = 256 / (D / 8);
   hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)),
                      dim3(256), 0, st, a);

@@ -115,6 +115,26 @@ __device__ __forceinline__ f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c) {
       0);
 }
 
+// The rows of one (batch, head) slice in the [rows, d] operand matrices: n
+// rows starting at row0.  Dense [B,H,N,d]: slice bh is rows bh*N ...  Packed
+// [H,total,d] (cu non-null): sequence b = bh / H of head h = bh % H starts at
+// row h*total + cu[b].  Boundaries are clamped into [0, total] and the
+// length to N (the longest sequence), so malformed boundaries cannot make a
+// kernel touch rows outside its head.
+struct SliceRows {
+  int n;
+  size_t row0;
+};
+
+__device__ __forceinline__ SliceRows slice_rows(const int32_t *cu, int total,
+                                                int N, int H, int bh) {
+  if (cu == nullptr) return {N, (size_t)bh * N};
+  const int b = bh / H, h = bh - b * H;
+  const int s = min(max(cu[b], 0), total);
+  const int e = min(max(cu[b + 1], s), total);
+  return {min(e - s, N), (size_t)h * total + s};
+}
+
 __device__ __forceinline__ u32x4 ldg128(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }

@@ -47,13 +47,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int bh = blockIdx.x % a.BH;
   const int qt = nqt - 1 - (int)(blockIdx.x / a.BH);
   const int b = bh / a.H;
-  const int N = a.N;
-  const size_t hoff = (size_t)bh * N * D;
+  const SliceRows sr = slice_rows(a.cu_seqlens, a.total, a.N, a.H, bh);
+  const int N = sr.n;
+  const size_t hoff = sr.row0 * D;
   const uint16_t *__restrict__ qg = (const uint16_t *)a.q + hoff;
   const uint16_t *__restrict__ kg = (const uint16_t *)a.k + hoff;
   const uint16_t *__restrict__ vg = (const uint16_t *)a.v + hoff;
 
   const int q0 = qt * BR;
+  if (q0 >= N) return;  // a packed sequence shorter than the longest one
   const int qw = q0 + wave * QPW;
   int kv_valid = N;
   if (PADDED) kv_valid = min(max(a.kv_len[b], 0), N);
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
           *reinterpret_cast<u32x2 *>(og + c0) = w2;
         }
       if (hh == 0 && a.m != nullptr) {
-        const size_t ri = (size_t)bh * N + qi;
+        const size_t ri = sr.row0 + qi;
         const float l_true =
             l_ref * fast_exp2((m_ref[qb] - m_max[qb]) * c);
         a.m[ri] = l_ref > 0.f ? m_max[qb] * a.scale : -INFINITY;
@@ -250,13 +252,15 @@ __global__ __launch_bounds__(64, 1) void fwd_f32_kernel(FwdArgs a) {
   const int bh = blockIdx.x % a.BH;
   const int qt = blockIdx.x / a.BH;
   const int b = bh / a.H;
-  const int N = a.N;
-  const size_t hoff = (size_t)bh * N * D;
+  const SliceRows sr = slice_rows(a.cu_seqlens, a.total, a.N, a.H, bh);
+  const int N = sr.n;
+  const size_t hoff = sr.row0 * D;
   const float *qg = (const float *)a.q + hoff;
   const float *kg = (const float *)a.k + hoff;
   const float *vg = (const float *)a.v + hoff;
   (void)nqt;
   const int qi = qt * 64 + tid;
+  if (qt * 64 >= N) return;  // a packed sequence shorter than the longest one
   int kv_valid = N;
   if (PADDED) kv_valid = min(max(a.kv_len[b], 0), N);
   int kend = kv_valid;
@@ -316,8 +320,8 @@ __global__ __launch_bounds__(64, 1) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < D; ++i) og[i] = o[i] * inv;
     if (a.m != nullptr) {
-      a.m[(size_t)bh * N + qi] = l_run > 0.f ? m_run * a.scale : -INFINITY;
-      a.l[(size_t)bh * N + qi] = l_run;
+      a.m[sr.row0 + qi] = l_run > 0.f ? m_run * a.scale : -INFINITY;
+      a.l[sr.row0 + qi] = l_run;
     }
   }
 }

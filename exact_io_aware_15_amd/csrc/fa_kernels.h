@@ -7,11 +7,17 @@
 
 namespace fa355 {
 
+// Dense problems use [B,H,N,d] matrices.  Packed variable-length problems
+// (cu_seqlens non-null) use [H,total,d]: sequence b of head h is rows
+// h*total + cu_seqlens[b] .. of those matrices, and N is the longest
+// sequence (it sizes the grid).
 struct FwdArgs {
-  const void *q, *k, *v;   // [B,H,N,d] bf16 or fp32
-  void *o;                 // [B,H,N,d]
-  float *m, *l;            // [B,H,N] or both null
-  const int32_t *kv_len;   // [B] or null
+  const void *q, *k, *v;   // [B,H,N,d] or [H,total,d], bf16 or fp32
+  void *o;
+  float *m, *l;            // [B,H,N] or [H,total], or both null
+  const int32_t *kv_len;   // [B] or null (dense only)
+  const int32_t *cu_seqlens;  // [B+1] or null
+  int total;               // packed rows per head (varlen)
   int B, H, N, BH;
   float scale;             // natural-units score scale
   float c;                 // scale * log2(e): scores enter exp2 in log2 units
@@ -23,9 +29,12 @@ hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal,
                           hipStream_t s);
 
 struct BwdArgs {
-  const uint16_t *q, *k, *v, *o, *dout;  // [B,H,N,d] bf16
-  const float *m, *l;                    // [B,H,N]
-  const int32_t *kv_len;                 // [B] or null
+  const uint16_t *q, *k, *v, *o, *dout;  // [B,H,N,d] or [H,total,d] bf16
+  const float *m, *l;                    // [B,H,N] or [H,total]
+  const int32_t *kv_len;                 // [B] or null (dense only)
+  const int32_t *cu_seqlens;             // [B+1] or null
+  int total;                             // packed rows per head (varlen)
+  long long rows;                        // rows of the [rows, d] matrices
   uint16_t *dq, *dk, *dv;                // [B,H,N,d] bf16
   float *lse2;                           // [B,H,N] workspace: log2-domain row offset
   float *delta;                          // [B,H,N] workspace: rowsum(dO*O)

@@ -122,6 +122,60 @@ int fa_bwd(int B, int H, int N, int d,
            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fa_fwd_varlen -- fa_fwd on a packed ragged batch (variable-length prefill).
+ * S12's NaN box: under a causal mask on a ragged batch whole tiles are
+ * routinely masked; the finite running-max start covers them.  The B
+ * sequences lie back to back along one token axis per head: sequence b is
+ * tokens cu_seqlens[b] .. cu_seqlens[b+1]-1, and a token attends only tokens
+ * of its own sequence (and, when causal, only those at or before it).
+ *
+ *   dtype, d, causal, scale, stream   as for fa_fwd.
+ *   B            sequences, >= 1.
+ *   H            heads, >= 1.
+ *   total        tokens per head, >= 0 (0: nothing to do, FA_OK; the
+ *                buffers may then be NULL).
+ *   max_seqlen   1 .. 1<<20, at least every sequence's length.
+ *   cu_seqlens   device int32 [B+1]: 0 = cu[0] <= cu[1] <= ... <= cu[B] =
+ *                total.  Boundaries outside [0, total] are clamped and
+ *                lengths above max_seqlen are cut to it, so malformed values
+ *                give unspecified results but no access outside the buffers.
+ *   q, k, v, o   [H, total, d] of `dtype` (head-major packed: head h's
+ *                tokens are rows h*total .. h*total+total-1); o written.
+ *   m, l         [H, total] fp32, written, or both NULL.
+ * Sequences of length 0 are allowed.  kv_len padding does not apply.
+ */
+int fa_fwd_varlen(int dtype, int B, int H, int total, int max_seqlen, int d,
+                  const int32_t *cu_seqlens, const void *q, const void *k,
+                  const void *v, void *o, float *m, float *l, int causal,
+                  float scale, void *stream);
+
+/*
+ * fa_bwd_varlen_workspace_bytes -- device workspace fa_bwd_varlen needs: two
+ * fp32 vectors [H, total], each padded to 256 bytes.  Returns 0 when total is
+ * 0 (no workspace needed) and for invalid sizes.
+ */
+size_t fa_bwd_varlen_workspace_bytes(int H, int total, int d);
+
+/*
+ * fa_bwd_varlen -- fa_bwd on a packed ragged batch (the layout and masking
+ * of fa_fwd_varlen; bf16 only).
+ *
+ *   B, H, total, max_seqlen, d, cu_seqlens, causal, scale   as for
+ *                     fa_fwd_varlen.
+ *   q, k, v, o, dout  [H, total, d] bf16; m, l [H, total] fp32 as written by
+ *                     fa_fwd_varlen for the same inputs.
+ *   dq, dk, dv        [H, total, d] bf16, written.
+ *   workspace         at least fa_bwd_varlen_workspace_bytes(H, total, d)
+ *                     bytes, 256-byte aligned (may be NULL when total = 0).
+ */
+int fa_bwd_varlen(int B, int H, int total, int max_seqlen, int d,
+                  const int32_t *cu_seqlens, const void *q, const void *k,
+                  const void *v, const void *o, const void *dout,
+                  const float *m, const float *l, int causal, float scale,
+                  void *dq, void *dk, void *dv, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
+/*
  * fa_decode_workspace_bytes -- device workspace fa_decode_paged needs: the
  * per-split partial triples (m, l, o) in fp32.  Returns 0 for invalid sizes.
  */

@@ -1,7 +1,7 @@
 """CPU checks of the C ABI: the library loads, exports every function that
 include/fa355.h declares, and rejects invalid arguments before launching
 anything.  No call here reaches a kernel launch (every call is invalid by
-construction), so these run without a GPU."""
+construction, or has no rows to compute), so these run without a GPU."""
 
 import ctypes
 import os
@@ -115,3 +115,44 @@ def test_last_hip_error_starts_clear(lib):
     assert _fwd(lib, q=NULL) == -1
     assert lib.fa_last_hip_error() == 0
     assert lib.fa_last_hip_error_str()
+
+
+def _fwd_varlen(lib, dtype=1, B=2, H=1, total=10, max_seqlen=8, d=64,
+                cu=FAKE, q=FAKE, m=NULL, l=NULL, scale=0.125):
+    return lib.fa_fwd_varlen(dtype, B, H, total, max_seqlen, d, cu, q, FAKE,
+                             FAKE, FAKE, m, l, 1, scale, NULL)
+
+
+def test_fwd_varlen_validation(lib):
+    assert _fwd_varlen(lib, cu=NULL) == -1
+    assert _fwd_varlen(lib, q=NULL) == -1
+    assert _fwd_varlen(lib, m=FAKE) == -1
+    assert _fwd_varlen(lib, B=0) == -2
+    assert _fwd_varlen(lib, total=-1) == -2
+    assert _fwd_varlen(lib, max_seqlen=0) == -2
+    assert _fwd_varlen(lib, max_seqlen=(1 << 20) + 1) == -2
+    assert _fwd_varlen(lib, H=1 << 12, total=1 << 20) == -2  # > 2^31 rows
+    assert _fwd_varlen(lib, scale=0.0) == -2
+    assert _fwd_varlen(lib, d=96) == -3
+    assert _fwd_varlen(lib, dtype=7) == -3
+    # no tokens: nothing to launch (no device is touched), NULL buffers fine
+    assert _fwd_varlen(lib, total=0) == 0
+    assert _fwd_varlen(lib, total=0, cu=NULL, q=NULL) == 0
+
+
+def test_bwd_varlen_workspace_and_validation(lib):
+    assert lib.fa_bwd_varlen_workspace_bytes(3, 1000, 64) == 2 * 12032
+    assert lib.fa_bwd_varlen_workspace_bytes(3, 0, 64) == 0
+    assert lib.fa_bwd_varlen_workspace_bytes(0, 10, 64) == 0
+    assert lib.fa_bwd_varlen_workspace_bytes(3, 10, 80) == 0
+
+    def call(cu=FAKE, total=1000, ws=FAKE, ws_bytes=1 << 20, d=64):
+        return lib.fa_bwd_varlen(2, 3, total, 600, d, cu, FAKE, FAKE, FAKE,
+                                 FAKE, FAKE, FAKE, FAKE, 1, 0.125, FAKE, FAKE,
+                                 FAKE, ws, ws_bytes, NULL)
+    assert call(cu=NULL) == -1
+    assert call(d=80) == -3
+    assert call(ws=NULL) == -4
+    assert call(ws_bytes=2 * 12032 - 1) == -4
+    assert call(ws=ctypes.c_void_p(0x1008)) == -4
+    assert call(total=0, ws=NULL, ws_bytes=0) == 0

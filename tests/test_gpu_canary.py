@@ -101,3 +101,32 @@ def test_decode_writes_stay_in_bounds():
                                     _stream())
     assert st == 0
     assert out.intact() and ws.intact()
+
+
+def test_varlen_malformed_boundaries_stay_in_bounds():
+    """cu_seqlens that decreases and overruns total: the kernels clamp each
+    sequence into [0, total], so every write stays inside the buffers (the
+    results themselves are unspecified)."""
+    import torch
+    H, total, d = 2, 100, 64
+    q, k, v = (to_device(normal((H, total, d), 87, t, "bf16"))
+               for t in range(3))
+    do = to_device(normal((H, total, d), 87, TID_DO, "bf16"))
+    cu = torch.tensor([0, 50, 30, 400], dtype=torch.int32, device="cuda")
+    o = Guarded(H * total * d * 2)
+    m = Guarded(H * total * 4)
+    l = Guarded(H * total * 4)
+    st = _lib.lib().fa_fwd_varlen(1, 3, H, total, 128, d, _p(cu), _p(q),
+                                  _p(k), _p(v), o.ptr, m.ptr, l.ptr, 1, 0.125,
+                                  _stream())
+    assert st == 0
+    assert o.intact() and m.intact() and l.intact()
+    grads = [Guarded(H * total * d * 2) for _ in range(3)]
+    wsb = _lib.lib().fa_bwd_varlen_workspace_bytes(H, total, d)
+    ws = Guarded(wsb)
+    st = _lib.lib().fa_bwd_varlen(3, H, total, 128, d, _p(cu), _p(q), _p(k),
+                                  _p(v), o.ptr, _p(do), m.ptr, l.ptr, 1, 0.125,
+                                  grads[0].ptr, grads[1].ptr, grads[2].ptr,
+                                  ws.ptr, wsb, _stream())
+    assert st == 0
+    assert all(g.intact() for g in grads) and ws.intact()

@@ -138,6 +138,8 @@ class Workload:
     qkv_mult: float = 1.0
     kv_len_range: Optional[tuple] = None   # (lo, hi) inclusive, key padding
     backward: bool = False
+    # varlen only: sequence lengths ~ U{lo..hi}; N is the longest allowed
+    seq_range: Optional[tuple] = None
     # decode only
     Hkv: int = 0
     ctx_range: Optional[tuple] = None
@@ -169,9 +171,32 @@ class Workload:
         q = normal((self.B, self.H, self.d), self.seed, TID_Q, self.dtype)
         return q, cache
 
+    def varlen_lens(self):
+        lo, hi = self.seq_range
+        return uniform_int(self.B, lo, hi, self.seed, TID_LEN)
+
+    def varlen_inputs(self):
+        """(cu_seqlens int32 [B+1], q, k, v [H, total, d]): the sequences
+        packed back to back along the token axis, head-major."""
+        lens = self.varlen_lens()
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        shape = (self.H, int(cu[-1]), self.d)
+        q, k, v = (normal(shape, self.seed, t, self.dtype, self.qkv_mult)
+                   for t in (TID_Q, TID_K, TID_V))
+        return cu, q, k, v
+
+    def varlen_dout(self):
+        total = int(np.sum(self.varlen_lens()))
+        return normal((self.H, total, self.d), self.seed, TID_DO, self.dtype)
+
     def fwd_flops(self):
-        """4*B*H*N^2*d, halved when causal (nominal N^2 under key padding)."""
-        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        """4*B*H*N^2*d, halved when causal (nominal N^2 under key padding);
+        for a packed ragged batch the sum of 4*H*L^2*d over its sequences."""
+        if self.kind == "varlen":
+            sq = float(np.sum(np.asarray(self.varlen_lens(), np.float64) ** 2))
+            f = 4.0 * self.H * sq * self.d
+        else:
+            f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
 
     def bwd_flops(self):
@@ -195,6 +220,11 @@ WORKLOADS = {
     "long_causal_16k_d128": Workload(
         "long_causal_16k_d128", 4, "attn", "bf16", 1, 16, 16384, 128,
         causal=True),
+    # A causal prefill batch packed without padding: 16 prompts of 64..4096
+    # tokens, GPT-2-medium-shaped heads.
+    "varlen_causal_prefill": Workload(
+        "varlen_causal_prefill", 6, "varlen", "bf16", 16, 16, 4096, 64,
+        causal=True, qkv_mult=0.5, backward=True, seq_range=(64, 4096)),
     "long_causal_64k_d64": Workload(
         "long_causal_64k_d64", 41, "attn", "bf16", 1, 2, 65536, 64,
         causal=True),
