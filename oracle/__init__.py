@@ -28,7 +28,8 @@ Modules:
   the split-K (m, l, o) merge of S12 exercise 1, and the S12 paged loop.
 * ``brute``     -- pure-Python scalar loops for tiny inputs.
 * ``varlen``    -- packed variable-length batches (block-diagonal visibility),
-  forward and backward.
+  forward and backward, and prefill of packed new tokens against a paged
+  cache.
 
 Pin status: every public function here is pinned by the CPU tests against
 closed forms, invariants, brute force or finite differences; none is marked
@@ -53,5 +54,6 @@ from .brute import brute_fwd  # noqa: F401
 from .varlen import (  # noqa: F401
     attention_bwd_varlen,
     attention_fwd_varlen,
+    prefill_paged,
     varlen_visible,
 )

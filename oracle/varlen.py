@@ -23,7 +23,8 @@ import math
 
 import numpy as np
 
-__all__ = ["varlen_visible", "attention_fwd_varlen", "attention_bwd_varlen"]
+__all__ = ["varlen_visible", "attention_fwd_varlen", "attention_bwd_varlen",
+           "prefill_paged"]
 
 
 def _scale(d, scale):
@@ -108,3 +109,56 @@ def attention_bwd_varlen(q, k, v, do, cu_seqlens, scale=None, causal=False,
             dk[h] += sc * (ds.T @ q[h, rr])
             D[h, rr] = Di
     return dq, dk, dv, D
+
+
+def prefill_paged(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q,
+                  scale=None, causal=True):
+    """Prefill of packed new tokens against a paged KV cache, by gather +
+    masked softmax (fp64).
+
+    S12's paged loop reads logical block t of a sequence from physical block
+    block_table[t], the last block holding n = min(block_size, seq_len -
+    t*block_size) tokens; GQA (S12 production paragraph): query head hq reads
+    KV head hq // (Hq/Hkv).  Readings: the cache already holds the K/V of
+    every one of the seq_lens[b] tokens of sequence b, including its new
+    ones; the new tokens are the last qlen_b = cu[b+1] - cu[b] positions, so
+    new token i sits at position seq_lens[b] - qlen_b + i and, when causal,
+    sees cached positions <= that one.
+
+    q: [Hq, total_q, d]; k_cache, v_cache: [num_blocks, Hkv, block_size, d];
+    block_table: [B, max_blocks]; seq_lens: [B].  Returns (o, m, l) with
+    o [Hq, total_q, d] and m, l [Hq, total_q] as in the dense definition.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    Hq, total_q, d = q.shape
+    Hkv, bs = k_cache.shape[1], k_cache.shape[2]
+    G = Hq // Hkv
+    sc = _scale(d, scale)
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    o = np.zeros((Hq, total_q, v_cache.shape[3]))
+    m = np.full((Hq, total_q), -np.inf)
+    l = np.zeros((Hq, total_q))
+    for b in range(cu.size - 1):
+        qs, qe = int(cu[b]), int(cu[b + 1])
+        L = int(seq_lens[b])
+        if qe == qs:
+            continue
+        kk, vv = [], []
+        for t in range(-(-L // bs)):
+            n = min(bs, L - t * bs)
+            phys = int(block_table[b, t])
+            kk.append(np.asarray(k_cache[phys, :, :n], dtype=np.float64))
+            vv.append(np.asarray(v_cache[phys, :, :n], dtype=np.float64))
+        Kb = np.concatenate(kk, axis=1) if kk else np.zeros((Hkv, 0, d))
+        Vb = np.concatenate(vv, axis=1) if vv else np.zeros((Hkv, 0, d))
+        pos = L - (qe - qs) + np.arange(qe - qs)
+        vis = np.ones((qe - qs, L), dtype=bool)
+        if causal:
+            vis &= np.arange(L)[None, :] <= pos[:, None]
+        for hq in range(Hq):
+            hk = hq // G
+            p, mm, ll = _softmax_rows(sc * (q[hq, qs:qe] @ Kb[hk].T), vis)
+            o[hq, qs:qe] = p @ Vb[hk]
+            m[hq, qs:qe] = mm
+            l[hq, qs:qe] = ll
+    return o, m, l

@@ -138,3 +138,95 @@ def test_varlen_backward_equals_dense_on_each_slice(causal):
                             do[None, :, s:e], None, causal)
         for got, want in zip((dq, dk, dv, D), ref):
             assert np.max(np.abs(got[:, s:e] - want[0])) <= 1e-12
+
+
+# ----------------------------------------------------------- paged prefill --
+
+from oracle import decode_paged, prefill_paged  # noqa: E402
+from workloads import paged_cache  # noqa: E402
+
+
+def _cache_from_packed(kp, vp, lens, bs, rng):
+    """Scatter packed per-sequence K/V [Hkv, total, d] into a shuffled
+    head-major cache [num_blocks, Hkv, bs, d]; returns (kc, vc, table)."""
+    Hkv, _, d = kp.shape
+    nblk = [-(-L // bs) for L in lens]
+    total_blocks = max(1, sum(nblk))
+    perm = rng.permutation(total_blocks)
+    kc = np.full((total_blocks, Hkv, bs, d), np.nan)
+    vc = np.full((total_blocks, Hkv, bs, d), np.nan)
+    table = np.full((len(lens), max(1, max(nblk))), -1)
+    off = tok = 0
+    for b, L in enumerate(lens):
+        for t in range(nblk[b]):
+            phys = perm[off + t]
+            table[b, t] = phys
+            n = min(bs, L - t * bs)
+            kc[phys, :, :n] = kp[:, tok + t * bs:tok + t * bs + n]
+            vc[phys, :, :n] = vp[:, tok + t * bs:tok + t * bs + n]
+        off += nblk[b]
+        tok += L
+    return kc, vc, table
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_from_empty_context_equals_varlen(causal):
+    rng = np.random.default_rng([41, int(causal)])
+    lens = [20, 1, 37, 16]
+    Hkv, G, d = 2, 2, 8
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    kp = rng.standard_normal((Hkv, cu[-1], d))
+    vp = rng.standard_normal((Hkv, cu[-1], d))
+    q = rng.standard_normal((Hkv * G, cu[-1], d))
+    kc, vc, table = _cache_from_packed(kp, vp, lens, 16, rng)
+    o, m, l = prefill_paged(q, kc, vc, table, lens, cu, None, causal)
+    ko, mo, lo = attention_fwd_varlen(q, np.repeat(kp, G, axis=0),
+                                      np.repeat(vp, G, axis=0), cu, None,
+                                      causal)
+    assert np.max(np.abs(o - ko)) <= 1e-13
+    assert np.max(np.abs(m - mo)) <= 1e-13
+    assert np.max(np.abs(l / lo - 1)) <= 1e-13
+
+
+def test_prefill_of_one_token_equals_paged_decode():
+    rng = np.random.default_rng(42)
+    lens = np.array([1, 17, 40, 100])
+    cache = paged_cache(lens, 2, 8, 16, 8, cfg_seed=43)
+    q = rng.standard_normal((4, 8, 8))          # [B, Hq, d] one token each
+    ref = decode_paged(q, cache.k_cache.exact, cache.v_cache.exact,
+                       cache.block_table, lens)
+    cu = np.arange(5)
+    o, _, _ = prefill_paged(q.transpose(1, 0, 2), cache.k_cache.exact,
+                            cache.v_cache.exact, cache.block_table, lens, cu,
+                            None, True)
+    assert np.max(np.abs(o.transpose(1, 0, 2) - ref)) <= 1e-13
+
+
+def test_prefill_matches_brute_force_with_context():
+    rng = np.random.default_rng(44)
+    L, qlen, d = 23, 6, 4
+    kp = rng.standard_normal((1, L, d))
+    vp = rng.standard_normal((1, L, d))
+    qfull = rng.standard_normal((L, d))
+    kc, vc, table = _cache_from_packed(kp, vp, [L], 4, rng)
+    o, _, _ = prefill_paged(qfull[None, L - qlen:], kc, vc, table, [L],
+                            [0, qlen], 0.6, True)
+    # brute force over every position; the new tokens are the last qlen rows
+    ref = brute_fwd(qfull.tolist(), kp[0].tolist(), vp[0].tolist(), 0.6, True)
+    assert np.max(np.abs(o[0] - np.array(ref[L - qlen:]))) <= 1e-13
+
+
+def test_prefill_is_invariant_to_moving_blocks():
+    rng = np.random.default_rng(45)
+    lens = np.array([33, 70])
+    cache = paged_cache(lens, 1, 8, 16, 5, cfg_seed=46)
+    cu = np.array([0, 9, 29])
+    q = rng.standard_normal((2, 29, 8))
+    kc, vc = cache.k_cache.exact, cache.v_cache.exact
+    o, _, _ = prefill_paged(q, kc, vc, cache.block_table, lens, cu)
+    perm = rng.permutation(kc.shape[0])
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm], vc2[perm] = kc, vc
+    table2 = np.where(cache.block_table >= 0, perm[cache.block_table], -1)
+    o2, _, _ = prefill_paged(q, kc2, vc2, table2, lens, cu)
+    assert np.array_equal(o, o2)
