@@ -214,6 +214,38 @@ def decode_bench(steps, warmup, splits=None):
                          "traffic": traffic_for("fa_decode_paged")}}
 
 
+def prefill_bench(steps, warmup):
+    """fa_prefill_paged on the chunked-prefill workload: TFLOP/s at
+    4*Hq*d per (new token, visible cached key)."""
+    import torch
+    import exact_io_aware_15_amd as fa
+    from workloads import WORKLOADS, to_device
+    w = WORKLOADS["paged_chunked_prefill"]
+    cu, q, cache = w.prefill_inputs(poison_tails=False)
+    qd = to_device(q)
+    kc, vc = to_device(cache.k_cache), to_device(cache.v_cache)
+    table = torch.from_numpy(cache.block_table).cuda()
+    lens = torch.from_numpy(cache.seq_lens).cuda()
+    cud = torch.from_numpy(cu).cuda()
+
+    def call():
+        return fa.prefill_paged(qd, kc, vc, table, lens, cud,
+                                w.seq_range[1], causal=True)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tf = w.prefill_flops() / ms / 1e9
+    return {"workload": w.name, "ms": round(ms, 4), "tflops": round(tf, 1),
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def sweep(steps, warmup):
     from workloads import WORKLOADS
     out = {}
@@ -234,6 +266,7 @@ def sweep(steps, warmup):
         out[name] = r
         del attn
     out["paged_gqa_decode"] = decode_bench(max(steps, 20), warmup)
+    out["paged_chunked_prefill"] = prefill_bench(max(steps, 20), warmup)
     return out
 
 

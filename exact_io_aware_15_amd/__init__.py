@@ -11,6 +11,8 @@ the library is missing, the calls raise.
     o, m, l = fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False)
     dq, dk, dv = bwd_varlen(q, k, v, o, do, m, l, cu_seqlens, max_seqlen)
     out = decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits=8)
+    o, m, l = prefill_paged(q, k_cache, v_cache, block_table, seq_lens,
+                            cu_seqlens_q, max_q, causal=True)
 """
 
 import math
@@ -18,6 +20,7 @@ import math
 from ._lib import FA_BF16, FA_F32, FaError, LibraryMissing, check, lib
 
 __all__ = ["fwd", "bwd", "fwd_varlen", "bwd_varlen", "decode_paged",
+           "prefill_paged",
            "bwd_workspace_bytes", "bwd_varlen_workspace_bytes",
            "decode_workspace_bytes", "FaError", "LibraryMissing"]
 
@@ -187,6 +190,45 @@ def bwd_varlen(q, k, v, o, do, m, l, cu_seqlens, max_seqlen, causal=False,
                                  _stream(q))
     check("fa_bwd_varlen", st)
     return dq, dk, dv
+
+
+def prefill_paged(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q,
+                  max_q, causal=True, scale=None, return_stats=True):
+    """New tokens of each sequence (packed [Hq, total_q, d] bf16) against a
+    paged cache [num_blocks, Hkv, 16, d] that already holds them; sequence
+    b's new tokens are its last cu[b+1]-cu[b] of seq_lens[b] positions.
+    Returns (o, m, l) with m, l fp32 [Hq, total_q]."""
+    torch = _torch()
+    Hq, total_q, d = q.shape
+    nb, Hkv, bs, dk = k_cache.shape
+    _check_dev("q", q, torch.bfloat16)
+    _check_dev("k_cache", k_cache, torch.bfloat16)
+    _check_dev("v_cache", v_cache, torch.bfloat16, k_cache.shape)
+    if dk != d:
+        raise ValueError("k_cache head dim differs from q")
+    _check_dev("block_table", block_table, torch.int32)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_blocks]")
+    B = block_table.shape[0]
+    _check_dev("seq_lens", seq_lens, torch.int32, (B,))
+    cu = _cu_seqlens(cu_seqlens_q, q.device)
+    if cu.numel() != B + 1:
+        raise ValueError("cu_seqlens_q must be [B+1]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    m = l = None
+    if return_stats:
+        m = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+        l = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib().fa_prefill_paged(B, Hq, Hkv, d, total_q, int(max_q),
+                                    _ptr(cu), _ptr(q), _ptr(k_cache),
+                                    _ptr(v_cache), nb, bs, _ptr(block_table),
+                                    block_table.shape[1], _ptr(seq_lens),
+                                    int(bool(causal)), scale, _ptr(o),
+                                    _ptr(m), _ptr(l), _stream(q))
+    check("fa_prefill_paged", st)
+    return o, m, l
 
 
 def decode_workspace_bytes(B, Hq, d, num_splits):

@@ -30,6 +30,8 @@ SIGNATURES = {
     "fa_bwd_varlen_workspace_bytes": (_Z, [_I, _I, _I]),
     "fa_bwd_varlen": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                            _P, _I, _F, _P, _P, _P, _P, _Z, _P]),
+    "fa_prefill_paged": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I,
+                              _I, _P, _I, _P, _I, _F, _P, _P, _P, _P]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "fa_decode_paged": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P,
                              _I, _F, _P, _P, _Z, _P]),

@@ -179,6 +179,42 @@ int fa_bwd_varlen(int B, int H, int total, int max_seqlen, int d,
   return from_hip(launch_bwd(a, d, causal != 0, (hipStream_t)stream));
 }
 
+int fa_prefill_paged(int B, int Hq, int Hkv, int d, int total_q, int max_q,
+                     const int32_t *cu_seqlens_q, const void *q,
+                     const void *k_cache, const void *v_cache, int num_blocks,
+                     int block_size, const int32_t *block_table,
+                     int max_blocks_per_seq, const int32_t *seq_lens,
+                     int causal, float scale, void *o, float *m, float *l,
+                     void *stream) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || num_blocks < 1 ||
+      max_blocks_per_seq < 1 || !valid_scale(scale))
+    return FA_E_SHAPE;
+  if (!varlen_shape_ok(B, Hq, total_q, max_q)) return FA_E_SHAPE;
+  if ((long long)B * max_blocks_per_seq > (1LL << 31) - 1 ||
+      (long long)max_blocks_per_seq * 16 > (1LL << 31) - 1 ||
+      (long long)num_blocks * block_size * Hkv * d > (1LL << 40))
+    return FA_E_SHAPE;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  if (block_size != 16) return FA_E_UNSUPPORTED;
+  if (total_q == 0) return FA_OK;  // no new tokens (empty buffers may be NULL)
+  if (!cu_seqlens_q || !q || !k_cache || !v_cache || !block_table ||
+      !seq_lens || !o)
+    return FA_E_NULLPTR;
+  if ((m == nullptr) != (l == nullptr)) return FA_E_NULLPTR;
+  FwdArgs a;
+  a.q = q; a.k = nullptr; a.v = nullptr; a.o = o; a.m = m; a.l = l;
+  a.kv_len = nullptr;
+  a.cu_seqlens = cu_seqlens_q; a.total = total_q;
+  a.k_cache = k_cache; a.v_cache = v_cache;
+  a.block_table = block_table; a.seq_lens = seq_lens;
+  a.max_blocks = max_blocks_per_seq; a.num_blocks = num_blocks; a.Hkv = Hkv;
+  a.B = B; a.H = Hq; a.N = max_q; a.BH = B * Hq;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  return from_hip(launch_prefill_paged(a, d, causal != 0,
+                                       (hipStream_t)stream));
+}
+
 size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
   if (B < 1 || Hq < 1 || (d != 64 && d != 128) || num_splits < 1 ||
       num_splits > 64)

@@ -322,6 +322,40 @@ __device__ __forceinline__ void dma_tile(uint16_t *tile, const uint16_t *src,
   }
 }
 
+// The same fill for a 64-row key or value tile of a paged cache: logical
+// row t of the tile is token t % 16 of cache block blk[t / 16], whose 16 x W
+// tile for this KV head starts at base + blk * blk_stride (base already
+// points at the head's tile inside block 0).  Rows past last_row read row
+// last_row.  blk[] holds valid block indices.
+template <int W>
+__device__ __forceinline__ void dma_tile_paged(uint16_t *tile,
+                                               const uint16_t *base,
+                                               size_t blk_stride,
+                                               const int (&blk)[4], int row0,
+                                               int last_row) {
+  constexpr int ROWS = 64;
+  constexpr int CPR = W / 8;
+  constexpr int SEGS = ROWS * W * 2 / 1024;
+  static_assert(SEGS % 4 == 0, "tile shape");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < SEGS / 4; ++u) {
+    const int seg = wave + 4 * u;
+    const int p = seg * 64 + lane;
+    const int r = p / CPR, phys = p % CPR;
+    const int t = min(row0 + ((r & ~31) | row_perm(r & 31)), last_row) - row0;
+    const int bi = t >> 4;
+    const int b = bi == 0 ? blk[0] : bi == 1 ? blk[1] : bi == 2 ? blk[2]
+                                                                 : blk[3];
+    const size_t goff = (size_t)b * blk_stride + (size_t)(t & 15) * W +
+                        (phys ^ lds_swz<W>(r)) * 8;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void *)(base + goff),
+        (__attribute__((address_space(3))) void *)(tile + seg * 512), 16, 0,
+        0);
+  }
+}
+
 __device__ __forceinline__ void wait_dma() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }

@@ -27,7 +27,7 @@ namespace {
 // reference, and l is converted to the true max at the end.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D, int QPW, bool CAUSAL, bool PADDED>
+template <int D, int QPW, bool CAUSAL, bool PADDED, bool PAGED = false>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int QB = QPW / 32;                    // 32-query blocks per wave
   constexpr int BR = 4 * QPW;                     // queries per workgroup
@@ -48,19 +48,36 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int qt = nqt - 1 - (int)(blockIdx.x / a.BH);
   const int b = bh / a.H;
   const SliceRows sr = slice_rows(a.cu_seqlens, a.total, a.N, a.H, bh);
-  const int N = sr.n;
+  const int N = sr.n;  // queries of this slice
   const size_t hoff = sr.row0 * D;
   const uint16_t *__restrict__ qg = (const uint16_t *)a.q + hoff;
-  const uint16_t *__restrict__ kg = (const uint16_t *)a.k + hoff;
-  const uint16_t *__restrict__ vg = (const uint16_t *)a.v + hoff;
+  const uint16_t *kg, *vg;
+  // Keys: the slice's own rows, or (paged prefill) the KV head's tiles in
+  // the cache, in which case the N queries are the last N of the kv_valid
+  // cached positions: query i sits at position i + qoff (causal offset).
+  int kv_valid, qoff = 0;
+  size_t blk_stride = 0;
+  const int32_t *btab = nullptr;
+  if (PAGED) {
+    const int h = bh - b * a.H, hk = h / (a.H / a.Hkv);
+    kv_valid = min(max(a.seq_lens[b], 0), a.max_blocks * 16);
+    qoff = kv_valid - N;
+    blk_stride = (size_t)a.Hkv * 16 * D;
+    kg = (const uint16_t *)a.k_cache + (size_t)hk * 16 * D;
+    vg = (const uint16_t *)a.v_cache + (size_t)hk * 16 * D;
+    btab = a.block_table + (size_t)b * a.max_blocks;
+  } else {
+    kg = (const uint16_t *)a.k + hoff;
+    vg = (const uint16_t *)a.v + hoff;
+    kv_valid = N;
+    if (PADDED) kv_valid = min(max(a.kv_len[b], 0), N);
+  }
 
   const int q0 = qt * BR;
   if (q0 >= N) return;  // a packed sequence shorter than the longest one
   const int qw = q0 + wave * QPW;
-  int kv_valid = N;
-  if (PADDED) kv_valid = min(max(a.kv_len[b], 0), N);
   int kend = kv_valid;
-  if (CAUSAL) kend = min(kend, q0 + BR);
+  if (CAUSAL) kend = max(0, min(kend, q0 + BR + qoff));
   const int ntiles = (kend + BC - 1) / BC;
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[q][16*ks + 8*hh + e] for
@@ -94,24 +111,47 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const float thr = kRescaleLog2 / c;  // threshold in raw score units
 
   // Global -> LDS staging by direct DMA; keys past kv_valid read the last
-  // valid key instead (finite data that the mask then excludes).
+  // valid key instead (finite data that the mask then excludes).  A paged
+  // tile takes its four cache blocks from the table (entries loaded one
+  // tile ahead of their use, clamped to valid block indices).
+  const int nb_used = (kv_valid + 15) / 16;
+  auto table_entries = [&](int t, int (&e)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = 4 * t + i;
+      e[i] = idx < nb_used ? min(max(btab[idx], 0), a.num_blocks - 1) : 0;
+    }
+  };
+  int e_next[4] = {0, 0, 0, 0};
   auto load_tile = [&](int k0, int buf) {
-    dma_tile<D, BC>(Ks[buf], kg, k0, kv_valid - 1);
-    dma_tile<D, BC>(Vs[buf], vg, k0, kv_valid - 1);
+    if (PAGED) {
+      dma_tile_paged<D>(Ks[buf], kg, blk_stride, e_next, k0, kv_valid - 1);
+      dma_tile_paged<D>(Vs[buf], vg, blk_stride, e_next, k0, kv_valid - 1);
+    } else {
+      dma_tile<D, BC>(Ks[buf], kg, k0, kv_valid - 1);
+      dma_tile<D, BC>(Vs[buf], vg, k0, kv_valid - 1);
+    }
   };
 
-  if (ntiles > 0) load_tile(0, 0);
+  if (ntiles > 0) {
+    if (PAGED) table_entries(0, e_next);
+    load_tile(0, 0);
+    if (PAGED) table_entries(1, e_next);
+  }
   wait_dma();
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * BC;
     const int buf = t & 1;
     // The other buffer was last read before the previous barrier.
-    if (t + 1 < ntiles) load_tile(k0 + BC, buf ^ 1);
+    if (t + 1 < ntiles) {
+      load_tile(k0 + BC, buf ^ 1);
+      if (PAGED) table_entries(t + 2, e_next);
+    }
     const uint16_t *Kt = Ks[buf];
     const uint16_t *Vt = Vs[buf];
 
-    if (!(CAUSAL && k0 > qw + QPW - 1)) {  // else: tile above the diagonal
+    if (!(CAUSAL && k0 > qw + QPW - 1 + qoff)) {  // else: above the diagonal
       // S^T = K Q^T for every (key block, query block).
       f32x16 s[QB][2];
 #pragma unroll
@@ -139,14 +179,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
         const int qbase = qw + 32 * qb;
         const int qi = qbase + ln;
         const bool need_mask =
-            (k0 + BC > kv_valid) || (CAUSAL && k0 + BC - 1 > qbase);
+            (k0 + BC > kv_valid) || (CAUSAL && k0 + BC - 1 > qbase + qoff);
         if (need_mask) {
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
-              const bool masked = key >= kv_valid || (CAUSAL && key > qi);
+              const bool masked =
+                  key >= kv_valid || (CAUSAL && key > qi + qoff);
               s[qb][kb][r] = masked ? -INFINITY : s[qb][kb][r];
             }
         }
@@ -365,6 +406,28 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool causal,
                   : fwd_bf16_dispatch_pad<64, false>(a, s);
   return causal ? fwd_bf16_dispatch_pad<128, true>(a, s)
                 : fwd_bf16_dispatch_pad<128, false>(a, s);
+}
+
+hipError_t launch_prefill_paged(const FwdArgs &a, int d, bool causal,
+                                hipStream_t s) {
+  const int nqt = (a.N + 127) / 128;
+  dim3 grid((unsigned)(nqt * a.BH)), block(256);
+  if (d == 64) {
+    if (causal)
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, 32, true, false, true>), grid,
+                         block, 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, 32, false, false, true>), grid,
+                         block, 0, s, a);
+  } else {
+    if (causal)
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, 32, true, false, true>), grid,
+                         block, 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, 32, false, false, true>), grid,
+                         block, 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal,

@@ -18,6 +18,12 @@ struct FwdArgs {
   const int32_t *kv_len;   // [B] or null (dense only)
   const int32_t *cu_seqlens;  // [B+1] or null
   int total;               // packed rows per head (varlen)
+  // Paged prefill: keys and values come from a paged cache
+  // [num_blocks, Hkv, 16, d] through block_table [B, max_blocks]; sequence
+  // b's queries are the last positions of its seq_lens[b] cached tokens.
+  const void *k_cache, *v_cache;
+  const int32_t *block_table, *seq_lens;
+  int max_blocks, num_blocks, Hkv;
   int B, H, N, BH;
   float scale;             // natural-units score scale
   float c;                 // scale * log2(e): scores enter exp2 in log2 units
@@ -25,6 +31,8 @@ struct FwdArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool causal,
                            hipStream_t s);
+hipError_t launch_prefill_paged(const FwdArgs &a, int d, bool causal,
+                                hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal,
                           hipStream_t s);
 

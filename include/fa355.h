@@ -176,6 +176,47 @@ int fa_bwd_varlen(int B, int H, int total, int max_seqlen, int d,
                   size_t workspace_bytes, void *stream);
 
 /*
+ * fa_prefill_paged -- exact attention of a packed chunk of new tokens per
+ * sequence against a paged KV cache (prefill / chunked prefill with a
+ * cached prefix).  S12's paged loop (logical block t of a sequence is
+ * physical block block_table[t]; the last block holds n = min(block_size,
+ * seq_len - t*block_size) tokens) with GQA head sharing (S12 production
+ * paragraph), run by the tiled forward of fa_fwd.
+ *
+ *   B              sequences (>= 1).
+ *   Hq, Hkv        query and KV heads; Hq % Hkv == 0, query head h reads KV
+ *                  head h / (Hq/Hkv).
+ *   d              64 or 128.
+ *   total_q        new tokens of all sequences (>= 0; 0: nothing to do).
+ *   max_q          1 .. 1<<20, at least every sequence's new-token count.
+ *   cu_seqlens_q   device int32 [B+1]: sequence b's new tokens are packed rows
+ *                  cu[b] .. cu[b+1]-1 (malformed values are clamped as for
+ *                  fa_fwd_varlen).
+ *   q, o           [Hq, total_q, d] bf16 (head-major packed); o written.
+ *   m, l           [Hq, total_q] fp32 written, or both NULL.
+ *   k_cache,
+ *   v_cache        [num_blocks, Hkv, block_size, d] bf16, holding the K/V of
+ *                  every token of each sequence, its new tokens included.
+ *   block_size     16.
+ *   block_table    device int32 [B, max_blocks_per_seq]; entries for t <
+ *                  ceil(seq_len/16) must be in [0, num_blocks) (others are
+ *                  clamped into that range, giving unspecified results).
+ *   seq_lens       device int32 [B]: cached tokens of sequence b, new ones
+ *                  included (clamped to max_blocks_per_seq * 16).  The new
+ *                  tokens are its last qlen_b = cu[b+1]-cu[b] positions: new
+ *                  token i sits at position seq_lens[b] - qlen_b + i.
+ *   causal         nonzero: a new token sees cached positions <= its own.
+ *   scale          finite, > 0.
+ */
+int fa_prefill_paged(int B, int Hq, int Hkv, int d, int total_q, int max_q,
+                     const int32_t *cu_seqlens_q, const void *q,
+                     const void *k_cache, const void *v_cache, int num_blocks,
+                     int block_size, const int32_t *block_table,
+                     int max_blocks_per_seq, const int32_t *seq_lens,
+                     int causal, float scale, void *o, float *m, float *l,
+                     void *stream);
+
+/*
  * fa_decode_workspace_bytes -- device workspace fa_decode_paged needs: the
  * per-split partial triples (m, l, o) in fp32.  Returns 0 for invalid sizes.
  */

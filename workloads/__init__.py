@@ -189,6 +189,35 @@ class Workload:
         total = int(np.sum(self.varlen_lens()))
         return normal((self.H, total, self.d), self.seed, TID_DO, self.dtype)
 
+    def prefill_inputs(self, poison_tails=True):
+        """Chunked prefill against a paged cache: context lengths ~ U(ctx),
+        new-token chunks ~ U(seq_range) (capped by the context); returns
+        (cu_seqlens_q, q [Hq, total_q, d], cache) where the cache holds all
+        seq_lens tokens, new ones included."""
+        ctx = uniform_int(self.B, self.ctx_range[0], self.ctx_range[1],
+                          self.seed, TID_LEN)
+        qlen = np.minimum(uniform_int(self.B, self.seq_range[0],
+                                      self.seq_range[1], self.seed, TID_PERM),
+                          ctx)
+        cu = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+        max_blocks = -(-self.ctx_range[1] // self.block_size)
+        cache = paged_cache(ctx, self.Hkv, self.d, self.block_size,
+                            max_blocks, self.seed, poison_tails)
+        q = normal((self.H, int(cu[-1]), self.d), self.seed, TID_Q,
+                   self.dtype)
+        return cu, q, cache
+
+    def prefill_flops(self):
+        """4*Hq*d per (new token, visible cached key): new token i of a
+        chunk of q tokens after c earlier ones sees c + i + 1 keys."""
+        cu, _, cache = self.prefill_inputs(poison_tails=False)
+        tot = 0.0
+        for b in range(self.B):
+            qn = int(cu[b + 1] - cu[b])
+            L = int(cache.seq_lens[b])
+            tot += qn * (L - qn) + qn * (qn + 1) / 2
+        return 4.0 * self.H * self.d * tot
+
     def fwd_flops(self):
         """4*B*H*N^2*d, halved when causal (nominal N^2 under key padding);
         for a packed ragged batch the sum of 4*H*L^2*d over its sequences."""
@@ -225,6 +254,11 @@ WORKLOADS = {
     "varlen_causal_prefill": Workload(
         "varlen_causal_prefill", 6, "varlen", "bf16", 16, 16, 4096, 64,
         causal=True, qkv_mult=0.5, backward=True, seq_range=(64, 4096)),
+    # Chunked prefill in serving: 8 sequences with 1K-8K cached tokens each,
+    # a new chunk of 256-1024 of them attending the whole prefix (GQA 4:1).
+    "paged_chunked_prefill": Workload(
+        "paged_chunked_prefill", 7, "prefill", "bf16", 8, 32, 1024, 128,
+        causal=True, Hkv=8, ctx_range=(1024, 8192), seq_range=(256, 1024)),
     "long_causal_64k_d64": Workload(
         "long_causal_64k_d64", 41, "attn", "bf16", 1, 2, 65536, 64,
         causal=True),
