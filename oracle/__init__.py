@@ -30,6 +30,8 @@ Modules:
 * ``varlen``    -- packed variable-length batches (block-diagonal visibility),
   forward and backward, and prefill of packed new tokens against a paged
   cache.
+* ``sparse``    -- block-sparse attention (exact under a block mask), forward
+  and backward.
 
 Pin status: every public function here is pinned by the CPU tests against
 closed forms, invariants, brute force or finite differences; none is marked
@@ -51,6 +53,11 @@ from .online import (  # noqa: F401
     paged_online,
 )
 from .brute import brute_fwd  # noqa: F401
+from .sparse import (  # noqa: F401
+    attention_bwd_block_sparse,
+    attention_fwd_block_sparse,
+    block_sparse_visible,
+)
 from .varlen import (  # noqa: F401
     attention_bwd_varlen,
     attention_fwd_varlen,
