@@ -112,6 +112,10 @@ class Attn:
         from workloads import to_device
         self.w, self.fa, self.torch = w, fa, torch
         self.varlen = w.kind == "varlen"
+        self.mask = None
+        if w.kind == "sparse":
+            from workloads import block_sparse_mask
+            self.mask = torch.from_numpy(block_sparse_mask(w.H, w.N)).cuda()
         if self.varlen:   # packed ragged batch, [H, total, d]
             cu, q, k, v = w.varlen_inputs()
             self.cu = torch.from_numpy(cu).cuda()
@@ -129,6 +133,9 @@ class Attn:
                               device="cuda")
 
     def fwd(self):
+        if self.mask is not None:
+            return self.fa.fwd_block_sparse(self.q, self.k, self.v, self.mask,
+                                            causal=self.w.causal)
         if self.varlen:
             return self.fa.fwd_varlen(self.q, self.k, self.v, self.cu,
                                       self.w.N, causal=self.w.causal)
@@ -136,6 +143,11 @@ class Attn:
                            kv_len=self.kv_len)
 
     def bwd(self, o, m, l):
+        if self.mask is not None:
+            return self.fa.bwd_block_sparse(self.q, self.k, self.v, o, self.do,
+                                            m, l, self.mask,
+                                            causal=self.w.causal,
+                                            workspace=self.ws)
         if self.varlen:
             return self.fa.bwd_varlen(self.q, self.k, self.v, o, self.do, m,
                                       l, self.cu, self.w.N,
@@ -251,7 +263,7 @@ def sweep(steps, warmup):
     out = {}
     for name in ["bert_large_padded", "gpt2_medium_causal_1k",
                  "long_causal_16k_d128", "long_causal_64k_d64",
-                 "varlen_causal_prefill"]:
+                 "varlen_causal_prefill", "block_sparse_16k"]:
         w = WORKLOADS[name]
         attn = Attn(w)
         step_ms, fwd_ms, bwd_ms, _ = time_step(attn, steps, warmup,
@@ -263,6 +275,15 @@ def sweep(steps, warmup):
             r["bwd_ms"] = round(bwd_ms, 4)
             r["bwd_tflops"] = round(w.bwd_flops() / bwd_ms / 1e9, 1)
             r["bwd_frac"] = round(r["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)
+        if w.kind == "sparse":   # the same shape without the mask
+            import dataclasses
+            dense = Attn(dataclasses.replace(w, kind="attn"))
+            _, dfwd, dbwd, _ = time_step(dense, steps, warmup, backward=True)
+            r["dense_fwd_ms"] = round(dfwd, 4)
+            r["dense_bwd_ms"] = round(dbwd, 4)
+            r["speedup_fwd"] = round(dfwd / fwd_ms, 2)
+            r["speedup_bwd"] = round(dbwd / bwd_ms, 2)
+            del dense
         out[name] = r
         del attn
     out["paged_gqa_decode"] = decode_bench(max(steps, 20), warmup)

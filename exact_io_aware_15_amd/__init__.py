@@ -19,7 +19,8 @@ import math
 
 from ._lib import FA_BF16, FA_F32, FaError, LibraryMissing, check, lib
 
-__all__ = ["fwd", "bwd", "fwd_varlen", "bwd_varlen", "decode_paged",
+__all__ = ["fwd", "bwd", "fwd_varlen", "bwd_varlen", "fwd_block_sparse",
+           "bwd_block_sparse", "decode_paged",
            "prefill_paged",
            "bwd_workspace_bytes", "bwd_varlen_workspace_bytes",
            "decode_workspace_bytes", "FaError", "LibraryMissing"]
@@ -121,6 +122,65 @@ def bwd(q, k, v, o, do, m, l, causal=False, kv_len=None, scale=None,
                           _ptr(dv), _ptr(workspace), workspace.numel(),
                           _stream(q))
     check("fa_bwd", st)
+    return dq, dk, dv
+
+
+def _block_mask(mask, H, N, device):
+    torch = _torch()
+    nb = (N + 127) // 128
+    _check_dev("block_mask", mask, torch.uint8, (H, nb, nb))
+    return mask
+
+
+def fwd_block_sparse(q, k, v, block_mask, causal=False, scale=None,
+                     return_stats=True):
+    """Block-sparse attention: q, k, v [B,H,N,d] bf16; block_mask uint8
+    [H, ceil(N/128), ceil(N/128)] (nonzero: the 128-query block attends the
+    128-key block).  Returns (o, m, l)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check_dev("q", q, torch.bfloat16)
+    _check_dev("k", k, q.dtype, q.shape)
+    _check_dev("v", v, q.dtype, q.shape)
+    block_mask = _block_mask(block_mask, H, N, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    m = l = None
+    if return_stats:
+        m = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        l = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib().fa_fwd_block_sparse(B, H, N, d, _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(o), _ptr(m), _ptr(l),
+                                       _ptr(block_mask), int(bool(causal)),
+                                       scale, _stream(q))
+    check("fa_fwd_block_sparse", st)
+    return o, m, l
+
+
+def bwd_block_sparse(q, k, v, o, do, m, l, block_mask, causal=False,
+                     scale=None, workspace=None):
+    """Gradients (dq, dk, dv) of fwd_block_sparse; bf16 [B,H,N,d]."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_dev(name, t, torch.bfloat16, (B, H, N, d))
+    _check_dev("m", m, torch.float32, (B, H, N))
+    _check_dev("l", l, torch.float32, (B, H, N))
+    block_mask = _block_mask(block_mask, H, N, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if workspace is None:
+        workspace = torch.empty(bwd_workspace_bytes(B, H, N, d),
+                                dtype=torch.uint8, device=q.device)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    with torch.cuda.device(q.device):
+        st = lib().fa_bwd_block_sparse(B, H, N, d, _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(o), _ptr(do), _ptr(m), _ptr(l),
+                                       _ptr(block_mask), int(bool(causal)),
+                                       scale, _ptr(dq), _ptr(dk), _ptr(dv),
+                                       _ptr(workspace), workspace.numel(),
+                                       _stream(q))
+    check("fa_bwd_block_sparse", st)
     return dq, dk, dv
 
 

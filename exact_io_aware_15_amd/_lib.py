@@ -25,6 +25,10 @@ SIGNATURES = {
     "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F,
                     _P, _P, _P, _P, _Z, _P]),
+    "fa_fwd_block_sparse": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
+                                 _I, _F, _P]),
+    "fa_bwd_block_sparse": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
+                                 _P, _I, _F, _P, _P, _P, _P, _Z, _P]),
     "fa_fwd_varlen": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                            _P, _I, _F, _P]),
     "fa_bwd_varlen_workspace_bytes": (_Z, [_I, _I, _I]),

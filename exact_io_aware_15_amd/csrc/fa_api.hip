@@ -73,7 +73,7 @@ int fa_fwd(int dtype, int B, int H, int N, int d, const void *q,
   if (!attn_shape_ok(B, H, N) || !valid_scale(scale)) return FA_E_SHAPE;
   if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
   if (dtype != FA_BF16 && dtype != FA_F32) return FA_E_UNSUPPORTED;
-  FwdArgs a;
+  FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.m = m; a.l = l; a.kv_len = kv_len;
   a.cu_seqlens = nullptr; a.total = 0;
   a.B = B; a.H = H; a.N = N; a.BH = B * H;
@@ -103,11 +103,59 @@ int fa_bwd(int B, int H, int N, int d, const void *q, const void *k,
   if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
   if (((uintptr_t)workspace) % kAlign) return FA_E_WORKSPACE;
   const size_t rows = (size_t)B * H * N;
-  BwdArgs a;
+  BwdArgs a{};
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k;
   a.v = (const uint16_t *)v; a.o = (const uint16_t *)o;
   a.dout = (const uint16_t *)dout; a.m = m; a.l = l; a.kv_len = kv_len;
   a.cu_seqlens = nullptr; a.total = 0; a.rows = (long long)rows;
+  a.dq = (uint16_t *)dq; a.dk = (uint16_t *)dk; a.dv = (uint16_t *)dv;
+  char *ws = (char *)workspace;
+  a.lse2 = (float *)ws;
+  a.delta = (float *)(ws + align_up(rows * sizeof(float)));
+  a.B = B; a.H = H; a.N = N; a.BH = B * H;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  return from_hip(launch_bwd(a, d, causal != 0, (hipStream_t)stream));
+}
+
+int fa_fwd_block_sparse(int B, int H, int N, int d, const void *q,
+                        const void *k, const void *v, void *o, float *m,
+                        float *l, const uint8_t *block_mask, int causal,
+                        float scale, void *stream) {
+  if (!q || !k || !v || !o || !block_mask) return FA_E_NULLPTR;
+  if ((m == nullptr) != (l == nullptr)) return FA_E_NULLPTR;
+  if (!attn_shape_ok(B, H, N) || !valid_scale(scale)) return FA_E_SHAPE;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.m = m; a.l = l;
+  a.block_mask = block_mask;
+  a.B = B; a.H = H; a.N = N; a.BH = B * H;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  return from_hip(launch_fwd_block_sparse(a, d, causal != 0,
+                                          (hipStream_t)stream));
+}
+
+int fa_bwd_block_sparse(int B, int H, int N, int d, const void *q,
+                        const void *k, const void *v, const void *o,
+                        const void *dout, const float *m, const float *l,
+                        const uint8_t *block_mask, int causal, float scale,
+                        void *dq, void *dk, void *dv, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !o || !dout || !m || !l || !dq || !dk || !dv ||
+      !block_mask)
+    return FA_E_NULLPTR;
+  if (!attn_shape_ok(B, H, N) || !valid_scale(scale)) return FA_E_SHAPE;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
+  if (((uintptr_t)workspace) % kAlign) return FA_E_WORKSPACE;
+  const size_t rows = (size_t)B * H * N;
+  BwdArgs a{};
+  a.q = (const uint16_t *)q; a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v; a.o = (const uint16_t *)o;
+  a.dout = (const uint16_t *)dout; a.m = m; a.l = l;
+  a.block_mask = block_mask; a.rows = (long long)rows;
   a.dq = (uint16_t *)dq; a.dk = (uint16_t *)dk; a.dv = (uint16_t *)dv;
   char *ws = (char *)workspace;
   a.lse2 = (float *)ws;
@@ -129,7 +177,7 @@ int fa_fwd_varlen(int dtype, int B, int H, int total, int max_seqlen, int d,
   if (total == 0) return FA_OK;  // no rows (empty buffers may be NULL)
   if (!cu_seqlens || !q || !k || !v || !o) return FA_E_NULLPTR;
   if ((m == nullptr) != (l == nullptr)) return FA_E_NULLPTR;
-  FwdArgs a;
+  FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.m = m; a.l = l; a.kv_len = nullptr;
   a.cu_seqlens = cu_seqlens; a.total = total;
   a.B = B; a.H = H; a.N = max_seqlen; a.BH = B * H;
@@ -164,7 +212,7 @@ int fa_bwd_varlen(int B, int H, int total, int max_seqlen, int d,
   if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
   if (((uintptr_t)workspace) % kAlign) return FA_E_WORKSPACE;
   const size_t rows = (size_t)H * total;
-  BwdArgs a;
+  BwdArgs a{};
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k;
   a.v = (const uint16_t *)v; a.o = (const uint16_t *)o;
   a.dout = (const uint16_t *)dout; a.m = m; a.l = l; a.kv_len = nullptr;
@@ -201,7 +249,7 @@ int fa_prefill_paged(int B, int Hq, int Hkv, int d, int total_q, int max_q,
       !seq_lens || !o)
     return FA_E_NULLPTR;
   if ((m == nullptr) != (l == nullptr)) return FA_E_NULLPTR;
-  FwdArgs a;
+  FwdArgs a{};
   a.q = q; a.k = nullptr; a.v = nullptr; a.o = o; a.m = m; a.l = l;
   a.kv_len = nullptr;
   a.cu_seqlens = cu_seqlens_q; a.total = total_q;
@@ -247,7 +295,7 @@ int fa_decode_paged(int B, int Hq, int Hkv, int d, const void *q,
   if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
   if (((uintptr_t)workspace) % kAlign) return FA_E_WORKSPACE;
   const size_t parts = (size_t)B * Hq * num_splits;
-  DecodeArgs a;
+  DecodeArgs a{};
   a.q = (const uint16_t *)q;
   a.k_cache = (const uint16_t *)k_cache;
   a.v_cache = (const uint16_t *)v_cache;

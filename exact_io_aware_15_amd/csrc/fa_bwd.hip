@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, bool PADDED>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     BwdArgs a) {
   constexpr int BC = 128;    // keys per workgroup, 32 per wave
@@ -143,12 +143,28 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     lv = ok ? lse2[q0 + tid] : INFINITY;
     dv2 = ok ? dlt[q0 + tid] : 0.f;
   };
+  // Query steps to visit: all from q_begin, or (block-sparse) those whose
+  // 128-query block the mask column of this 128-key block allows.
+  const int nsteps = (N + BR - 1) / BR;
+  MaskWalk walk;
+  if (SPARSE) {
+    const int nb = (a.N + 127) / 128;
+    const int h = bh - b * a.H;
+    walk.mask = a.block_mask + (size_t)h * nb * nb + kt;
+    walk.stride = nb;
+    walk.per = 128 / BR;
+    walk.n = nsteps;
+  }
+  auto next_step = [&](int st) { return SPARSE ? walk.next(st) : st; };
+
   float l_nx = 0.f, d_nx = 0.f;
-  if (q_begin < N) {
-    dma_tile<D, BR>(Qs[0], qg, q_begin, N - 1);
-    dma_tile<D, BR>(dOs[0], dog, q_begin, N - 1);
+  int st = next_step(q_begin / BR);
+  if (st < nsteps) {
+    const int q1 = st * BR;
+    dma_tile<D, BR>(Qs[0], qg, q1, N - 1);
+    dma_tile<D, BR>(dOs[0], dog, q1, N - 1);
     if (tid < BR) {
-      load_stats(q_begin, l_nx, d_nx);
+      load_stats(q1, l_nx, d_nx);
       LDs[0][2 * tid] = l_nx;
       LDs[0][2 * tid + 1] = d_nx;
     }
@@ -156,13 +172,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   wait_dma();
   __syncthreads();
 
-  int buf = 0;
-  for (int q0 = q_begin; q0 < N; q0 += BR, buf ^= 1) {
-    const bool has_next = q0 + BR < N;
+  for (int buf = 0; st < nsteps; buf ^= 1) {
+    const int q0 = st * BR;
+    const int sn = next_step(st + 1);
+    const bool has_next = sn < nsteps;
     if (has_next) {  // the other buffers were last read before the barrier
-      dma_tile<D, BR>(Qs[buf ^ 1], qg, q0 + BR, N - 1);
-      dma_tile<D, BR>(dOs[buf ^ 1], dog, q0 + BR, N - 1);
-      if (tid < BR) load_stats(q0 + BR, l_nx, d_nx);
+      dma_tile<D, BR>(Qs[buf ^ 1], qg, sn * BR, N - 1);
+      dma_tile<D, BR>(dOs[buf ^ 1], dog, sn * BR, N - 1);
+      if (tid < BR) load_stats(sn * BR, l_nx, d_nx);
     }
     const uint16_t *Qt = Qs[buf];
     const uint16_t *dOt = dOs[buf];
@@ -238,6 +255,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     }
     wait_dma();
     __syncthreads();
+    st = sn;
   }
 
   // Epilogue: dK = scale * dK_acc, dV; lane = column, registers = key rows.
@@ -256,7 +274,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     }
 }
 
-template <int D, bool CAUSAL, bool PADDED>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
     BwdArgs a) {
   constexpr int BR = 128;    // queries per workgroup, 32 per wave
@@ -314,18 +332,32 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
 
   // Double-buffered K / V tiles (DMA); keys past kv_valid read the last
   // valid key (finite data that the mask excludes).
-  if (ntiles > 0) {
-    dma_tile<D, BC>(Ks[0], kg, 0, kv_valid - 1);
-    dma_tile<D, BC>(Vs[0], vg, 0, kv_valid - 1);
+  // Key tiles to visit: all, or (block-sparse) those whose 128-key block
+  // the mask row of this 128-query block allows.
+  MaskWalk walk;
+  if (SPARSE) {
+    const int nb = (a.N + 127) / 128;
+    const int h = bh - b * a.H;
+    walk.mask = a.block_mask + ((size_t)h * nb + qt) * nb;
+    walk.stride = 1;
+    walk.per = 128 / BC;
+    walk.n = ntiles;
+  }
+  auto next_tile = [&](int t) { return SPARSE ? walk.next(t) : t; };
+
+  int t = next_tile(0);
+  if (t < ntiles) {
+    dma_tile<D, BC>(Ks[0], kg, t * BC, kv_valid - 1);
+    dma_tile<D, BC>(Vs[0], vg, t * BC, kv_valid - 1);
   }
   wait_dma();
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  for (int buf = 0; t < ntiles; buf ^= 1) {
     const int k0 = t * BC;
-    const int buf = t & 1;
-    if (t + 1 < ntiles) {  // the other buffer was last read before the barrier
-      dma_tile<D, BC>(Ks[buf ^ 1], kg, k0 + BC, kv_valid - 1);
-      dma_tile<D, BC>(Vs[buf ^ 1], vg, k0 + BC, kv_valid - 1);
+    const int tn = next_tile(t + 1);
+    if (tn < ntiles) {  // the other buffer was last read before the barrier
+      dma_tile<D, BC>(Ks[buf ^ 1], kg, tn * BC, kv_valid - 1);
+      dma_tile<D, BC>(Vs[buf ^ 1], vg, tn * BC, kv_valid - 1);
     }
     const uint16_t *Kt = Ks[buf];
     const uint16_t *Vt = Vs[buf];
@@ -387,6 +419,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
     }
     wait_dma();  // the next tile has landed
     __syncthreads();
+    t = tn;
   }
 
   if (qi < N) {
@@ -405,13 +438,13 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool PADDED>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false>
 void bwd_launch_main(const BwdArgs &a, hipStream_t st) {
   const int nkt = (a.N + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED>),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED, SPARSE>),
                      dim3((unsigned)(nkt * a.BH)), dim3(256), 0, st, a);
   const int nqt = (a.N + 127) / 128;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED>),
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED, SPARSE>),
                      dim3((unsigned)(nqt * a.BH)), dim3(256), 0, st, a);
 }
 
@@ -421,7 +454,9 @@ hipError_t bwd_dispatch(const BwdArgs &a, hipStream_t st) {
   const int rpb = 256 / (D / 8);
   hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)),
                      dim3(256), 0, st, a);
-  if (a.kv_len)
+  if (a.block_mask)
+    bwd_launch_main<D, CAUSAL, false, true>(a, st);
+  else if (a.kv_len)
     bwd_launch_main<D, CAUSAL, true>(a, st);
   else
     bwd_launch_main<D, CAUSAL, false>(a, st);

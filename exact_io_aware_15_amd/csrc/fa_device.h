@@ -356,6 +356,37 @@ __device__ __forceinline__ void dma_tile_paged(uint16_t *tile,
   }
 }
 
+// Walks the allowed 128-wide blocks of one row (or column) of a block mask
+// in order.  The wave loads 64 mask bytes at once, one per lane, and keeps
+// them as a 64-bit ballot; next(t) is then a scalar bit scan except when a
+// 64-block window is crossed.  Block b's byte is at mask[b * stride]; units
+// (tiles or steps) of `per` per block, n units in all.  Uniform control flow.
+struct MaskWalk {
+  const uint8_t *mask;
+  int stride, per, n;
+  int win0 = -1;
+  uint64_t bits = 0;
+
+  __device__ __forceinline__ int next(int t) {
+    while (t < n) {
+      const int b = t / per, w0 = b & ~63;
+      if (w0 != win0) {
+        const int bl = w0 + (int)(threadIdx.x & 63);
+        const bool ok = bl * per < n && mask[(size_t)bl * stride] != 0;
+        bits = __ballot(ok);
+        win0 = w0;
+      }
+      const uint64_t rest = bits >> (b - w0);
+      if (rest) {
+        const int nb = b + __builtin_ctzll(rest);
+        return max(nb * per, t);
+      }
+      t = (w0 + 64) * per;
+    }
+    return n;
+  }
+};
+
 __device__ __forceinline__ void wait_dma() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }

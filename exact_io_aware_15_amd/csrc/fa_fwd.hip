@@ -27,7 +27,8 @@ namespace {
 // reference, and l is converted to the true max at the end.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D, int QPW, bool CAUSAL, bool PADDED, bool PAGED = false>
+template <int D, int QPW, bool CAUSAL, bool PADDED, bool PAGED = false,
+          bool SPARSE = false>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int QB = QPW / 32;                    // 32-query blocks per wave
   constexpr int BR = 4 * QPW;                     // queries per workgroup
@@ -133,20 +134,34 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  if (ntiles > 0) {
-    if (PAGED) table_entries(0, e_next);
-    load_tile(0, 0);
-    if (PAGED) table_entries(1, e_next);
+  // Tiles to visit: all of [0, ntiles), or (block-sparse) those whose
+  // 128-key block the mask row of this 128-query block allows.
+  MaskWalk walk;
+  if (SPARSE) {
+    const int nb = (a.N + 127) / 128;
+    const int h = bh - b * a.H;
+    walk.mask = a.block_mask + ((size_t)h * nb + qt) * nb;
+    walk.stride = 1;
+    walk.per = 128 / BC;
+    walk.n = ntiles;
+  }
+  auto next_tile = [&](int t) { return SPARSE ? walk.next(t) : t; };
+
+  int t = next_tile(0);
+  if (t < ntiles) {
+    if (PAGED) table_entries(t, e_next);
+    load_tile(t * BC, 0);
+    if (PAGED) table_entries(t + 1, e_next);
   }
   wait_dma();
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  for (int buf = 0; t < ntiles; buf ^= 1) {
     const int k0 = t * BC;
-    const int buf = t & 1;
+    const int tn = next_tile(t + 1);
     // The other buffer was last read before the previous barrier.
-    if (t + 1 < ntiles) {
-      load_tile(k0 + BC, buf ^ 1);
-      if (PAGED) table_entries(t + 2, e_next);
+    if (tn < ntiles) {
+      load_tile(tn * BC, buf ^ 1);
+      if (PAGED) table_entries(tn + 1, e_next);
     }
     const uint16_t *Kt = Ks[buf];
     const uint16_t *Vt = Vs[buf];
@@ -247,6 +262,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 
     wait_dma();  // the next tile has landed
     __syncthreads();
+    t = tn;
   }
 
   // Epilogue: O = o / l (0 for a row with no visible key); m in natural
@@ -406,6 +422,29 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool causal,
                   : fwd_bf16_dispatch_pad<64, false>(a, s);
   return causal ? fwd_bf16_dispatch_pad<128, true>(a, s)
                 : fwd_bf16_dispatch_pad<128, false>(a, s);
+}
+
+hipError_t launch_fwd_block_sparse(const FwdArgs &a, int d, bool causal,
+                                   hipStream_t s) {
+  const int nqt = (a.N + 127) / 128;
+  dim3 grid((unsigned)(nqt * a.BH)), block(256);
+  if (d == 64) {
+    if (causal)
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, 32, true, false, false, true>),
+                         grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, 32, false, false, false, true>),
+                         grid, block, 0, s, a);
+  } else {
+    if (causal)
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, 32, true, false, false, true>),
+                         grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL(
+          (fwd_bf16_kernel<128, 32, false, false, false, true>), grid, block,
+          0, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill_paged(const FwdArgs &a, int d, bool causal,

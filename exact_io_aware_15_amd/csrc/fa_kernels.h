@@ -24,6 +24,9 @@ struct FwdArgs {
   const void *k_cache, *v_cache;
   const int32_t *block_table, *seq_lens;
   int max_blocks, num_blocks, Hkv;
+  // Block-sparse: block_mask [H, nb, nb] uint8 over 128 x 128 blocks
+  // (nb = ceil(N / 128)); nonzero = query block i attends key block j.
+  const uint8_t *block_mask;
   int B, H, N, BH;
   float scale;             // natural-units score scale
   float c;                 // scale * log2(e): scores enter exp2 in log2 units
@@ -33,6 +36,8 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int d, bool causal,
                            hipStream_t s);
 hipError_t launch_prefill_paged(const FwdArgs &a, int d, bool causal,
                                 hipStream_t s);
+hipError_t launch_fwd_block_sparse(const FwdArgs &a, int d, bool causal,
+                                   hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal,
                           hipStream_t s);
 
@@ -43,6 +48,7 @@ struct BwdArgs {
   const int32_t *cu_seqlens;             // [B+1] or null
   int total;                             // packed rows per head (varlen)
   long long rows;                        // rows of the [rows, d] matrices
+  const uint8_t *block_mask;             // [H, nb, nb] or null (see FwdArgs)
   uint16_t *dq, *dk, *dv;                // [B,H,N,d] bf16
   float *lse2;                           // [B,H,N] workspace: log2-domain row offset
   float *delta;                          // [B,H,N] workspace: rowsum(dO*O)

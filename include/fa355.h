@@ -122,6 +122,38 @@ int fa_bwd(int B, int H, int N, int d,
            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fa_fwd_block_sparse -- block-sparse attention (FA notes §4.4): the score
+ * matrix is cut into 128 x 128 blocks and only the blocks the mask allows
+ * are computed; masked blocks are skipped, not loaded.  Exact attention
+ * under the mask (an approximation of full attention).  bf16 only.
+ *
+ *   B, H, N, d, q, k, v, o, m, l, causal, scale, stream   as for fa_fwd
+ *                (dtype bf16).
+ *   block_mask   device uint8 [H, nb, nb], nb = ceil(N / 128), shared by
+ *                the batch: nonzero at [h, i, j] lets queries 128i .. see
+ *                keys 128j .. (also subject to the causal rule).  A query
+ *                row left with no visible key gets o = 0, l = 0, m = -inf.
+ */
+int fa_fwd_block_sparse(int B, int H, int N, int d, const void *q,
+                        const void *k, const void *v, void *o, float *m,
+                        float *l, const uint8_t *block_mask, int causal,
+                        float scale, void *stream);
+
+/*
+ * fa_bwd_block_sparse -- gradients of fa_fwd_block_sparse (the chain rule
+ * of fa_bwd under the mask; masked blocks are skipped).  Arguments as for
+ * fa_bwd without kv_len, plus the same block_mask; the workspace is
+ * fa_bwd_workspace_bytes(B, H, N, d) bytes.  Keys no query sees get
+ * dk = dv = 0; queries that see no key get dq = 0.
+ */
+int fa_bwd_block_sparse(int B, int H, int N, int d, const void *q,
+                        const void *k, const void *v, const void *o,
+                        const void *dout, const float *m, const float *l,
+                        const uint8_t *block_mask, int causal, float scale,
+                        void *dq, void *dk, void *dv, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
  * fa_fwd_varlen -- fa_fwd on a packed ragged batch (variable-length prefill).
  * S12's NaN box: under a causal mask on a ragged batch whole tiles are
  * routinely masked; the finite running-max start covers them.  The B

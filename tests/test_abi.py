@@ -156,3 +156,22 @@ def test_bwd_varlen_workspace_and_validation(lib):
     assert call(ws_bytes=2 * 12032 - 1) == -4
     assert call(ws=ctypes.c_void_p(0x1008)) == -4
     assert call(total=0, ws=NULL, ws_bytes=0) == 0
+
+
+def test_block_sparse_validation(lib):
+    def fwd(q=FAKE, mask=FAKE, N=300, d=64, m=NULL):
+        return lib.fa_fwd_block_sparse(1, 2, N, d, q, FAKE, FAKE, FAKE, m,
+                                       NULL, mask, 0, 0.125, NULL)
+    assert fwd(mask=NULL) == -1
+    assert fwd(q=NULL) == -1
+    assert fwd(m=FAKE) == -1
+    assert fwd(N=0) == -2
+    assert fwd(d=96) == -3
+
+    def bwd(mask=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return lib.fa_bwd_block_sparse(1, 2, 300, 64, FAKE, FAKE, FAKE, FAKE,
+                                       FAKE, FAKE, FAKE, mask, 1, 0.125, FAKE,
+                                       FAKE, FAKE, ws, ws_bytes, NULL)
+    assert bwd(mask=NULL) == -1
+    assert bwd(ws=NULL) == -4
+    assert bwd(ws_bytes=16) == -4

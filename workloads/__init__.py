@@ -91,6 +91,17 @@ class Paged:
     block_size: int
 
 
+def block_sparse_mask(H, N, band=2, stride=8):
+    """Structured 128 x 128 block mask [H, nb, nb] (uint8): a local band
+    |i - j| <= band plus every stride-th key block (global columns), the
+    same for every head."""
+    nb = -(-N // 128)
+    i = np.arange(nb)[:, None]
+    j = np.arange(nb)[None, :]
+    m = (np.abs(i - j) <= band) | (j % stride == 0)
+    return np.broadcast_to(m.astype(np.uint8), (H, nb, nb)).copy()
+
+
 def paged_cache(seq_lens, Hkv, d, block_size, max_blocks, cfg_seed,
                 poison_tails=True):
     """Random paged cache: every sequence's blocks are a slice of one random
@@ -224,6 +235,12 @@ class Workload:
         if self.kind == "varlen":
             sq = float(np.sum(np.asarray(self.varlen_lens(), np.float64) ** 2))
             f = 4.0 * self.H * sq * self.d
+        elif self.kind == "sparse":   # computed (unmasked) blocks only
+            mask = block_sparse_mask(self.H, self.N)
+            rows = np.minimum(128, self.N - 128 * np.arange(mask.shape[1]))
+            cnt = float(np.einsum("hij,i,j->", mask.astype(np.float64), rows,
+                                  rows))
+            f = 4.0 * self.B * cnt * self.d
         else:
             f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2 if self.causal else f
@@ -259,6 +276,11 @@ WORKLOADS = {
     "paged_chunked_prefill": Workload(
         "paged_chunked_prefill", 7, "prefill", "bf16", 8, 32, 1024, 128,
         causal=True, Hkv=8, ctx_range=(1024, 8192), seq_range=(256, 1024)),
+    # Block-sparse attention at 16K: a 5-block local band plus every 8th key
+    # block (about 16% of the blocks), non-causal.
+    "block_sparse_16k": Workload(
+        "block_sparse_16k", 8, "sparse", "bf16", 1, 16, 16384, 64,
+        qkv_mult=0.5, backward=True),
     "long_causal_64k_d64": Workload(
         "long_causal_64k_d64", 41, "attn", "bf16", 1, 2, 65536, 64,
         causal=True),
