@@ -32,6 +32,8 @@ Modules:
   cache.
 * ``sparse``    -- block-sparse attention (exact under a block mask), forward
   and backward.
+* ``dropout``   -- dropout on the probability matrix (FA notes §2.1 / §3.4)
+  with a counter-based generator (Philox4x32-10), forward and backward.
 
 Pin status: every public function here is pinned by the CPU tests against
 closed forms, invariants, brute force or finite differences; none is marked
@@ -53,6 +55,13 @@ from .online import (  # noqa: F401
     paged_online,
 )
 from .brute import brute_fwd  # noqa: F401
+from .dropout import (  # noqa: F401
+    attention_bwd_dropout,
+    attention_fwd_dropout,
+    dropout_keep,
+    dropout_threshold,
+    philox4x32_10,
+)
 from .sparse import (  # noqa: F401
     attention_bwd_block_sparse,
     attention_fwd_block_sparse,
