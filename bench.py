@@ -139,6 +139,10 @@ class Attn:
         if self.varlen:
             return self.fa.fwd_varlen(self.q, self.k, self.v, self.cu,
                                       self.w.N, causal=self.w.causal)
+        if self.w.p_drop > 0:
+            return self.fa.fwd_dropout(self.q, self.k, self.v, self.w.p_drop,
+                                       self.w.seed, 0, causal=self.w.causal,
+                                       kv_len=self.kv_len)
         return self.fa.fwd(self.q, self.k, self.v, causal=self.w.causal,
                            kv_len=self.kv_len)
 
@@ -152,6 +156,11 @@ class Attn:
             return self.fa.bwd_varlen(self.q, self.k, self.v, o, self.do, m,
                                       l, self.cu, self.w.N,
                                       causal=self.w.causal, workspace=self.ws)
+        if self.w.p_drop > 0:
+            return self.fa.bwd_dropout(self.q, self.k, self.v, o, self.do, m,
+                                       l, self.w.p_drop, self.w.seed, 0,
+                                       causal=self.w.causal,
+                                       kv_len=self.kv_len, workspace=self.ws)
         return self.fa.bwd(self.q, self.k, self.v, o, self.do, m, l,
                            causal=self.w.causal, kv_len=self.kv_len,
                            workspace=self.ws)
@@ -263,7 +272,8 @@ def sweep(steps, warmup):
     out = {}
     for name in ["bert_large_padded", "gpt2_medium_causal_1k",
                  "long_causal_16k_d128", "long_causal_64k_d64",
-                 "varlen_causal_prefill", "block_sparse_16k"]:
+                 "varlen_causal_prefill", "block_sparse_16k",
+                 "gpt2_medium_causal_4k_dropout"]:
         w = WORKLOADS[name]
         attn = Attn(w)
         step_ms, fwd_ms, bwd_ms, _ = time_step(attn, steps, warmup,
@@ -275,6 +285,15 @@ def sweep(steps, warmup):
             r["bwd_ms"] = round(bwd_ms, 4)
             r["bwd_tflops"] = round(w.bwd_flops() / bwd_ms / 1e9, 1)
             r["bwd_frac"] = round(r["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)
+        if w.p_drop > 0:   # the same inputs without dropout
+            import dataclasses
+            plain = Attn(dataclasses.replace(w, p_drop=0.0))
+            _, pfwd, pbwd, _ = time_step(plain, steps, warmup, backward=True)
+            r["no_dropout_fwd_ms"] = round(pfwd, 4)
+            r["no_dropout_bwd_ms"] = round(pbwd, 4)
+            r["dropout_cost_fwd"] = round(fwd_ms / pfwd, 3)
+            r["dropout_cost_bwd"] = round(bwd_ms / pbwd, 3)
+            del plain
         if w.kind == "sparse":   # the same shape without the mask
             import dataclasses
             dense = Attn(dataclasses.replace(w, kind="attn"))

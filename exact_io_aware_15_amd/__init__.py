@@ -19,7 +19,8 @@ import math
 
 from ._lib import FA_BF16, FA_F32, FaError, LibraryMissing, check, lib
 
-__all__ = ["fwd", "bwd", "fwd_varlen", "bwd_varlen", "fwd_block_sparse",
+__all__ = ["fwd", "bwd", "fwd_dropout", "bwd_dropout", "fwd_varlen",
+           "bwd_varlen", "fwd_block_sparse",
            "bwd_block_sparse", "decode_paged",
            "prefill_paged",
            "bwd_workspace_bytes", "bwd_varlen_workspace_bytes",
@@ -122,6 +123,64 @@ def bwd(q, k, v, o, do, m, l, causal=False, kv_len=None, scale=None,
                           _ptr(dv), _ptr(workspace), workspace.numel(),
                           _stream(q))
     check("fa_bwd", st)
+    return dq, dk, dv
+
+
+def fwd_dropout(q, k, v, p_drop, seed, offset=0, causal=False, kv_len=None,
+                scale=None, return_stats=True):
+    """Attention forward with dropout on P fused in: q, k, v [B,H,N,d] bf16.
+
+    Element (i, j) of head b*H + h is kept iff its Philox4x32-10 byte (counter
+    (i, group(j), b*H + h, offset), key = seed) is >= round(256 p_drop); kept
+    probabilities are scaled by 256 / (256 - round(256 p_drop)).  Returns
+    (o, m, l) with the pre-dropout softmax statistics m, l.
+    """
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check_dev("q", q, torch.bfloat16)
+    _check_dev("k", k, q.dtype, q.shape)
+    _check_dev("v", v, q.dtype, q.shape)
+    kv_len = _kv_len(kv_len, B, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    m = l = None
+    if return_stats:
+        m = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        l = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib().fa_fwd_dropout(B, H, N, d, _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(o), _ptr(m), _ptr(l), _ptr(kv_len),
+                                  int(bool(causal)), scale, float(p_drop),
+                                  int(seed), int(offset), _stream(q))
+    check("fa_fwd_dropout", st)
+    return o, m, l
+
+
+def bwd_dropout(q, k, v, o, do, m, l, p_drop, seed, offset=0, causal=False,
+                kv_len=None, scale=None, workspace=None):
+    """Gradients (dq, dk, dv) of fwd_dropout with the same p_drop, seed and
+    offset (the mask is regenerated on chip); all bf16 [B,H,N,d]."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_dev(name, t, torch.bfloat16, (B, H, N, d))
+    _check_dev("m", m, torch.float32, (B, H, N))
+    _check_dev("l", l, torch.float32, (B, H, N))
+    kv_len = _kv_len(kv_len, B, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if workspace is None:
+        workspace = torch.empty(bwd_workspace_bytes(B, H, N, d),
+                                dtype=torch.uint8, device=q.device)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    with torch.cuda.device(q.device):
+        st = lib().fa_bwd_dropout(B, H, N, d, _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(o), _ptr(do), _ptr(m), _ptr(l),
+                                  _ptr(kv_len), int(bool(causal)), scale,
+                                  float(p_drop), int(seed), int(offset),
+                                  _ptr(dq), _ptr(dk), _ptr(dv),
+                                  _ptr(workspace), workspace.numel(),
+                                  _stream(q))
+    check("fa_bwd_dropout", st)
     return dq, dk, dv
 
 

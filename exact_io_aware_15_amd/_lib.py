@@ -16,6 +16,7 @@ STATUS = {0: "FA_OK", -1: "FA_E_NULLPTR", -2: "FA_E_SHAPE",
 
 # Every function the header declares, with its ctypes signature.
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_U64, _U32 = ctypes.c_uint64, ctypes.c_uint32
 SIGNATURES = {
     "fa_status_str": (ctypes.c_char_p, [_I]),
     "fa_last_hip_error": (_I, []),
@@ -25,6 +26,10 @@ SIGNATURES = {
     "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F,
                     _P, _P, _P, _P, _Z, _P]),
+    "fa_fwd_dropout": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I,
+                            _F, _F, _U64, _U32, _P]),
+    "fa_bwd_dropout": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                            _I, _F, _F, _U64, _U32, _P, _P, _P, _P, _Z, _P]),
     "fa_fwd_block_sparse": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                  _I, _F, _P]),
     "fa_bwd_block_sparse": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,

@@ -43,6 +43,58 @@ int from_hip(hipError_t e) {
   return FA_E_HIP;
 }
 
+// Dropout parameters: thr = floor(256 p + 1/2), exact in double (256 p is
+// exact for a float p); valid for p >= 0 with thr <= 255.
+bool drop_setup(float p, uint64_t seed, uint32_t offset, Dropout &dr) {
+  if (!(p >= 0.f)) return false;  // also rejects NaN
+  const double t = floor((double)p * 256.0 + 0.5);
+  if (t > 255.0) return false;
+  dr.thr = (uint32_t)t;
+  dr.keep_scale = (float)(256.0 / (256.0 - t));
+  dr.seed_lo = (uint32_t)seed;
+  dr.seed_hi = (uint32_t)(seed >> 32);
+  dr.offset = offset;
+  return true;
+}
+
+int fwd_dense(int dtype, int B, int H, int N, int d, const void *q,
+              const void *k, const void *v, void *o, float *m, float *l,
+              const int32_t *kv_len, int causal, float scale,
+              const Dropout &dr, void *stream) {
+  FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.m = m; a.l = l; a.kv_len = kv_len;
+  a.cu_seqlens = nullptr; a.total = 0;
+  a.drop = dr;
+  a.B = B; a.H = H; a.N = N; a.BH = B * H;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == FA_BF16) return from_hip(launch_fwd_bf16(a, d, causal != 0, s));
+  return from_hip(launch_fwd_f32(a, d, causal != 0, s));
+}
+
+int bwd_dense(int B, int H, int N, int d, const void *q, const void *k,
+              const void *v, const void *o, const void *dout, const float *m,
+              const float *l, const int32_t *kv_len, int causal, float scale,
+              const Dropout &dr, void *dq, void *dk, void *dv,
+              void *workspace, void *stream) {
+  const size_t rows = (size_t)B * H * N;
+  BwdArgs a{};
+  a.q = (const uint16_t *)q; a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v; a.o = (const uint16_t *)o;
+  a.dout = (const uint16_t *)dout; a.m = m; a.l = l; a.kv_len = kv_len;
+  a.cu_seqlens = nullptr; a.total = 0; a.rows = (long long)rows;
+  a.drop = dr;
+  a.dq = (uint16_t *)dq; a.dk = (uint16_t *)dk; a.dv = (uint16_t *)dv;
+  char *ws = (char *)workspace;
+  a.lse2 = (float *)ws;
+  a.delta = (float *)(ws + align_up(rows * sizeof(float)));
+  a.B = B; a.H = H; a.N = N; a.BH = B * H;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  return from_hip(launch_bwd(a, d, causal != 0, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -73,15 +125,24 @@ int fa_fwd(int dtype, int B, int H, int N, int d, const void *q,
   if (!attn_shape_ok(B, H, N) || !valid_scale(scale)) return FA_E_SHAPE;
   if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
   if (dtype != FA_BF16 && dtype != FA_F32) return FA_E_UNSUPPORTED;
-  FwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.o = o; a.m = m; a.l = l; a.kv_len = kv_len;
-  a.cu_seqlens = nullptr; a.total = 0;
-  a.B = B; a.H = H; a.N = N; a.BH = B * H;
-  a.scale = scale;
-  a.c = (float)((double)scale * 1.4426950408889634);
-  hipStream_t s = (hipStream_t)stream;
-  if (dtype == FA_BF16) return from_hip(launch_fwd_bf16(a, d, causal != 0, s));
-  return from_hip(launch_fwd_f32(a, d, causal != 0, s));
+  return fwd_dense(dtype, B, H, N, d, q, k, v, o, m, l, kv_len, causal, scale,
+                   Dropout{}, stream);
+}
+
+int fa_fwd_dropout(int B, int H, int N, int d, const void *q, const void *k,
+                   const void *v, void *o, float *m, float *l,
+                   const int32_t *kv_len, int causal, float scale,
+                   float p_drop, uint64_t seed, uint32_t offset,
+                   void *stream) {
+  if (!q || !k || !v || !o) return FA_E_NULLPTR;
+  if ((m == nullptr) != (l == nullptr)) return FA_E_NULLPTR;
+  Dropout dr{};
+  if (!attn_shape_ok(B, H, N) || !valid_scale(scale) ||
+      !drop_setup(p_drop, seed, offset, dr))
+    return FA_E_SHAPE;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  return fwd_dense(FA_BF16, B, H, N, d, q, k, v, o, m, l, kv_len, causal,
+                   scale, dr, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -102,20 +163,28 @@ int fa_bwd(int B, int H, int N, int d, const void *q, const void *k,
   const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
   if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
   if (((uintptr_t)workspace) % kAlign) return FA_E_WORKSPACE;
-  const size_t rows = (size_t)B * H * N;
-  BwdArgs a{};
-  a.q = (const uint16_t *)q; a.k = (const uint16_t *)k;
-  a.v = (const uint16_t *)v; a.o = (const uint16_t *)o;
-  a.dout = (const uint16_t *)dout; a.m = m; a.l = l; a.kv_len = kv_len;
-  a.cu_seqlens = nullptr; a.total = 0; a.rows = (long long)rows;
-  a.dq = (uint16_t *)dq; a.dk = (uint16_t *)dk; a.dv = (uint16_t *)dv;
-  char *ws = (char *)workspace;
-  a.lse2 = (float *)ws;
-  a.delta = (float *)(ws + align_up(rows * sizeof(float)));
-  a.B = B; a.H = H; a.N = N; a.BH = B * H;
-  a.scale = scale;
-  a.c = (float)((double)scale * 1.4426950408889634);
-  return from_hip(launch_bwd(a, d, causal != 0, (hipStream_t)stream));
+  return bwd_dense(B, H, N, d, q, k, v, o, dout, m, l, kv_len, causal, scale,
+                   Dropout{}, dq, dk, dv, workspace, stream);
+}
+
+int fa_bwd_dropout(int B, int H, int N, int d, const void *q, const void *k,
+                   const void *v, const void *o, const void *dout,
+                   const float *m, const float *l, const int32_t *kv_len,
+                   int causal, float scale, float p_drop, uint64_t seed,
+                   uint32_t offset, void *dq, void *dk, void *dv,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+  if (!q || !k || !v || !o || !dout || !m || !l || !dq || !dk || !dv)
+    return FA_E_NULLPTR;
+  Dropout dr{};
+  if (!attn_shape_ok(B, H, N) || !valid_scale(scale) ||
+      !drop_setup(p_drop, seed, offset, dr))
+    return FA_E_SHAPE;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
+  if (((uintptr_t)workspace) % kAlign) return FA_E_WORKSPACE;
+  return bwd_dense(B, H, N, d, q, k, v, o, dout, m, l, kv_len, causal, scale,
+                   dr, dq, dk, dv, workspace, stream);
 }
 
 int fa_fwd_block_sparse(int B, int H, int N, int d, const void *q,

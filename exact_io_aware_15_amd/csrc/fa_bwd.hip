@@ -64,7 +64,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false,
+          bool DROP = false>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     BwdArgs a) {
   constexpr int BC = 128;    // keys per workgroup, 32 per wave
@@ -203,6 +204,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
       // The mask test is wave-uniform: a scalar branch picks the variant.
       const bool need_mask =
           (kw + 32 > kv_valid) || (CAUSAL && qs < kw + 31);
+      // Dropout keep bits of this key's 16 queries (bit 16*(r/8) + r%8).
+      uint32_t kbits = 0;
+      if (DROP)
+        kbits = drop_keep_transposed(
+            drop_bytes(a.drop, qs + ln, 2 * (kw >> 5) + hh, bh), a.drop.thr,
+            ln, hh);
       uint32_t pp[8], ps[8];
       auto probs = [&](auto masked_tile) {
 #pragma unroll
@@ -221,8 +228,17 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                   key >= kv_valid || (CAUSAL && key > q0 + qo0 + t);
               p = masked ? 0.f : p;
             }
-            pv[t] = p;
-            dsv[t] = p * (dp[r] - st[2 * t + 1]);
+            if (DROP) {
+              // dV takes the kept P (scaled in the epilogue); dP passes
+              // through the same mask and scale before the softmax rule.
+              const bool kp = (kbits >> (16 * (r >> 3) + (r & 7))) & 1u;
+              pv[t] = kp ? p : 0.f;
+              dsv[t] = p * fmaf(dp[r], kp ? a.drop.keep_scale : 0.f,
+                                -st[2 * t + 1]);
+            } else {
+              pv[t] = p;
+              dsv[t] = p * (dp[r] - st[2 * t + 1]);
+            }
           }
           pp[i] = pack_bf16x2(pv[0], pv[1]);
           ps[i] = pack_bf16x2(dsv[0], dsv[1]);
@@ -258,7 +274,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     st = sn;
   }
 
-  // Epilogue: dK = scale * dK_acc, dV; lane = column, registers = key rows.
+  // Epilogue: dK = scale * dK_acc, dV (times the dropout keep scale);
+  // lane = column, registers = key rows.
+  const float vscale = DROP ? a.drop.keep_scale : 1.0f;
 #pragma unroll
   for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -267,14 +285,15 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
       if (kr < N) {
         const size_t idx = (size_t)kr * D + cb * 32 + ln;
         const __bf16 kv = (__bf16)(dk[cb][r] * a.scale);
-        const __bf16 vv = (__bf16)dv[cb][r];
+        const __bf16 vv = (__bf16)(DROP ? dv[cb][r] * vscale : dv[cb][r]);
         dkg[idx] = __builtin_bit_cast(uint16_t, kv);
         dvg[idx] = __builtin_bit_cast(uint16_t, vv);
       }
     }
 }
 
-template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false,
+          bool DROP = false>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
     BwdArgs a) {
   constexpr int BR = 128;    // queries per workgroup, 32 per wave
@@ -379,6 +398,10 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
         // mask test is wave-uniform: a scalar branch picks the variant.
         const bool need_mask =
             (k0 + BC > kv_valid) || (CAUSAL && k0 + BC - 1 > qw);
+        // Dropout: register r uses byte r of this lane's call for (query,
+        // group 2*(key block) + hh).
+        u32x4 rnd = {0u, 0u, 0u, 0u};
+        if (DROP) rnd = drop_bytes(a.drop, qi, 2 * ((k0 >> 5) + kb) + hh, bh);
         auto grads = [&](auto masked_tile) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
@@ -393,7 +416,14 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
                 const bool masked = kk >= kv_valid || (CAUSAL && kk > qi);
                 p = masked ? 0.f : p;
               }
-              dsv[u] = p * (dp[r] - drow);
+              if (DROP)
+                dsv[u] = p * fmaf(dp[r],
+                                  drop_keep(rnd, r, a.drop.thr)
+                                      ? a.drop.keep_scale
+                                      : 0.f,
+                                  -drow);
+              else
+                dsv[u] = p * (dp[r] - drow);
             }
             ps[kb][i] = pack_bf16x2(dsv[0], dsv[1]);
           }
@@ -438,13 +468,14 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false>
+template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false,
+          bool DROP = false>
 void bwd_launch_main(const BwdArgs &a, hipStream_t st) {
   const int nkt = (a.N + 127) / 128;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED, SPARSE>),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED, SPARSE, DROP>),
                      dim3((unsigned)(nkt * a.BH)), dim3(256), 0, st, a);
   const int nqt = (a.N + 127) / 128;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED, SPARSE>),
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED, SPARSE, DROP>),
                      dim3((unsigned)(nqt * a.BH)), dim3(256), 0, st, a);
 }
 
@@ -456,6 +487,10 @@ hipError_t bwd_dispatch(const BwdArgs &a, hipStream_t st) {
                      dim3(256), 0, st, a);
   if (a.block_mask)
     bwd_launch_main<D, CAUSAL, false, true>(a, st);
+  else if (a.drop.thr != 0 && a.kv_len)
+    bwd_launch_main<D, CAUSAL, true, false, true>(a, st);
+  else if (a.drop.thr != 0)
+    bwd_launch_main<D, CAUSAL, false, false, true>(a, st);
   else if (a.kv_len)
     bwd_launch_main<D, CAUSAL, true>(a, st);
   else

@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_kernels.h"
+
 namespace fa355 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -386,6 +388,74 @@ struct MaskWalk {
     return n;
   }
 };
+
+// ---------------------------------------------------------------------------
+// Dropout on P.  The pages fuse it into the kernel but give no generator; the
+// keep decision of element (query i, key j) of head bh comes from Philox4x32
+// with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers:
+// As Easy as 1, 2, 3", SC 2011).  One call per (row, 16-key group):
+//   counter (i, g, bh, offset), key (seed low word, seed high word),
+//   g = 2*(j/32) + (j/8)%2, and j uses byte t = 8*((j/16)%2) + j%8 of the
+// 16 output bytes (byte t = bits 8*(t%4).. of word t/4).  The element is kept
+// iff that byte >= thr; kept values are scaled by 256/(256 - thr).  In the
+// 32x32 score layout where a lane owns one query and, for key block kb, the
+// keys 16*(r/8) + 8*hh + r%8 (r = 0..15), register r uses byte r of the
+// lane's call for group 2*kb + hh.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1,
+                                               uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;  // Weyl key increments
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// The 16 random bytes of (row, group) for head bh.
+__device__ __forceinline__ u32x4 drop_bytes(const Dropout &dr, int row,
+                                            int group, int bh) {
+  return philox4x32_10((uint32_t)row, (uint32_t)group, (uint32_t)bh,
+                       dr.offset, dr.seed_lo, dr.seed_hi);
+}
+
+// Keep decision of byte r (0..15) of a call's output.
+__device__ __forceinline__ bool drop_keep(const u32x4 &w, int r,
+                                          uint32_t thr) {
+  return ((w[r >> 2] >> (8 * (r & 3))) & 0xffu) >= thr;
+}
+
+// Transposed keep bits for a lane that owns one KEY of a 32x32 block and, in
+// register r, the query 16*(r/8) + 8*hh + r%8 (the key-stationary layout).
+// Every lane first draws the call its lane would own in the query-per-lane
+// layout (query ln, group half hh: w); the 16 keep bits are then exchanged
+// across the wave with ballots.  Ballot t has bit L = keep(query L%32, key
+// 16*(t/8) + 8*(L/32) + t%8).  Key kl needs ballot t(kl) = 8*((kl/16)%2) +
+// kl%8, word half (kl/8)%2, which each lane selects for itself.  Returns a
+// word whose bit 16*(r/8) + r%8 is the keep decision of register r.  Call
+// with all 64 lanes active.
+__device__ __forceinline__ uint32_t drop_keep_transposed(const u32x4 &w,
+                                                         uint32_t thr, int ln,
+                                                         int hh) {
+  const int my_t = 8 * ((ln >> 4) & 1) + (ln & 7);
+  const bool high = (ln >> 3) & 1;
+  uint32_t word = 0;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const uint64_t bt = __ballot(drop_keep(w, t, thr));
+    const uint32_t half = high ? (uint32_t)(bt >> 32) : (uint32_t)bt;
+    word = my_t == t ? half : word;
+  }
+  return word >> (8 * hh);
+}
 
 __device__ __forceinline__ void wait_dma() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -28,7 +28,7 @@ namespace {
 constexpr float kRescaleLog2 = 8.0f;
 
 template <int D, int QPW, bool CAUSAL, bool PADDED, bool PAGED = false,
-          bool SPARSE = false>
+          bool SPARSE = false, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int QB = QPW / 32;                    // 32-query blocks per wave
   constexpr int BR = 4 * QPW;                     // queries per workgroup
@@ -227,6 +227,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
             for (int r = 0; r < 16; ++r) oacc[qb][cb][r] *= alpha;
         }
         const float mc = m_ref[qb] * c;
+        // Dropout: this lane's 16 random bytes per key block (its query,
+        // group 2*(key block) + hh); l keeps the undropped sum.
+        u32x4 rnd[2];
+        if (DROP) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            rnd[kb] = drop_bytes(a.drop, qi, 2 * ((k0 >> 5) + kb) + hh, bh);
+        }
         float lsum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -237,8 +245,16 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
               const int r = 8 * s2 + 2 * i;
               const float p0 = fast_exp2(fmaf(s[qb][kb][r], c, -mc));
               const float p1 = fast_exp2(fmaf(s[qb][kb][r + 1], c, -mc));
-              pv[qb][kb][s2][i] = pack_bf16x2(p0, p1);
-              lsum = dot2_ones(pv[qb][kb][s2][i], lsum);
+              const uint32_t pu = pack_bf16x2(p0, p1);
+              lsum = dot2_ones(pu, lsum);
+              if (DROP) {
+                const uint32_t keep =
+                    (drop_keep(rnd[kb], r, a.drop.thr) ? 0xffffu : 0u) |
+                    (drop_keep(rnd[kb], r + 1, a.drop.thr) ? 0xffff0000u : 0u);
+                pv[qb][kb][s2][i] = pu & keep;
+              } else {
+                pv[qb][kb][s2][i] = pu;
+              }
             }
         l_run[qb] += lsum;
       }
@@ -272,7 +288,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     const int qi = qw + 32 * qb + ln;
     const float l_ref = sum_xor32(l_run[qb]);
     if (qi < N) {
-      const float inv = l_ref > 0.f ? 1.0f / l_ref : 0.f;
+      // Kept probabilities carry the factor 256 / (256 - thr).
+      const float num = DROP ? a.drop.keep_scale : 1.0f;
+      const float inv = l_ref > 0.f ? num / l_ref : 0.f;
       uint16_t *og = (uint16_t *)a.o + hoff + (size_t)qi * D;
 #pragma unroll
       for (int cb = 0; cb < D / 32; ++cb)
@@ -391,12 +409,24 @@ hipError_t fwd_bf16_dispatch_pad(const FwdArgs &a, hipStream_t s) {
   constexpr int QPW = 32;
   const int nqt = (a.N + 4 * QPW - 1) / (4 * QPW);
   dim3 grid((unsigned)(nqt * a.BH)), block(256);
-  if (a.kv_len)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QPW, CAUSAL, true>), grid, block, 0,
-                       s, a);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, QPW, CAUSAL, false>), grid, block,
-                       0, s, a);
+  const bool drop = a.drop.thr != 0;
+  if (a.kv_len) {
+    if (drop)
+      hipLaunchKernelGGL(
+          (fwd_bf16_kernel<D, QPW, CAUSAL, true, false, false, true>), grid,
+          block, 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, QPW, CAUSAL, true>), grid, block,
+                         0, s, a);
+  } else {
+    if (drop)
+      hipLaunchKernelGGL(
+          (fwd_bf16_kernel<D, QPW, CAUSAL, false, false, false, true>), grid,
+          block, 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, QPW, CAUSAL, false>), grid, block,
+                         0, s, a);
+  }
   return hipGetLastError();
 }
 

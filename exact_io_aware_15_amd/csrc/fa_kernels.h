@@ -7,6 +7,14 @@
 
 namespace fa355 {
 
+// Dropout on the probabilities (keep iff a Philox byte >= thr; see
+// fa_device.h).  thr = 0 means no dropout.
+struct Dropout {
+  uint32_t thr;       // 0..255
+  float keep_scale;   // 256 / (256 - thr)
+  uint32_t seed_lo, seed_hi, offset;
+};
+
 // Dense problems use [B,H,N,d] matrices.  Packed variable-length problems
 // (cu_seqlens non-null) use [H,total,d]: sequence b of head h is rows
 // h*total + cu_seqlens[b] .. of those matrices, and N is the longest
@@ -27,6 +35,7 @@ struct FwdArgs {
   // Block-sparse: block_mask [H, nb, nb] uint8 over 128 x 128 blocks
   // (nb = ceil(N / 128)); nonzero = query block i attends key block j.
   const uint8_t *block_mask;
+  Dropout drop;            // dense bf16 only
   int B, H, N, BH;
   float scale;             // natural-units score scale
   float c;                 // scale * log2(e): scores enter exp2 in log2 units
@@ -49,6 +58,7 @@ struct BwdArgs {
   int total;                             // packed rows per head (varlen)
   long long rows;                        // rows of the [rows, d] matrices
   const uint8_t *block_mask;             // [H, nb, nb] or null (see FwdArgs)
+  Dropout drop;                          // dense only (see FwdArgs)
   uint16_t *dq, *dk, *dv;                // [B,H,N,d] bf16
   float *lse2;                           // [B,H,N] workspace: log2-domain row offset
   float *delta;                          // [B,H,N] workspace: rowsum(dO*O)

@@ -122,6 +122,57 @@ int fa_bwd(int B, int H, int N, int d,
            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fa_fwd_dropout -- fa_fwd (bf16) with dropout on the probability matrix,
+ * fused into the kernel: FA notes §2.1 counts dropout on P among the
+ * memory-bound element-wise steps of standard attention and §3.4 lists it
+ * among the operations done on chip, so the dropped matrix never reaches HBM.
+ * The pages fix no generator.  This library draws the keep decisions from
+ * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As
+ * Easy as 1, 2, 3", SC 2011), a counter-based generator, so that the backward
+ * pass regenerates the same mask instead of storing it:
+ *   for head bh = b*H + h, query i, key j:
+ *     g = 2*(j/32) + (j/8)%2,   t = 8*((j/16)%2) + j%8,
+ *     words = Philox4x32-10(counter (i, g, bh, offset),
+ *                           key (seed & 0xffffffff, seed >> 32)),
+ *     byte  = bits 8*(t%4) .. 8*(t%4)+7 of words[t/4],
+ *     keep(i, j) = byte >= T,   T = floor(256 p_drop + 1/2).
+ *   O = (P * keep * 256/(256 - T)) V with P the softmax of the visible
+ *   scores; so the drop probability is T/256 exactly (p_drop rounded to a
+ *   multiple of 1/256) and the output is unbiased.
+ *
+ *   B, H, N, d, q, k, v, o, kv_len, causal, scale, stream   as for fa_fwd
+ *                 (dtype bf16).
+ *   m, l          as for fa_fwd: the statistics of the softmax BEFORE
+ *                 dropout (what fa_bwd_dropout needs), or both NULL.
+ *   p_drop        drop probability, 0 <= p_drop and T <= 255 (p_drop <
+ *                 255.5/256); otherwise FA_E_SHAPE.  p_drop = 0 gives the
+ *                 results of fa_fwd exactly.
+ *   seed, offset  the generator's key and fourth counter word: calls that
+ *                 differ in either draw independent masks.
+ */
+int fa_fwd_dropout(int B, int H, int N, int d, const void *q, const void *k,
+                   const void *v, void *o, float *m, float *l,
+                   const int32_t *kv_len, int causal, float scale,
+                   float p_drop, uint64_t seed, uint32_t offset,
+                   void *stream);
+
+/*
+ * fa_bwd_dropout -- gradients of fa_fwd_dropout with the same (p_drop, seed,
+ * offset): the mask is regenerated on chip, not read.  With Z = keep *
+ * 256/(256 - T):  dV = (P*Z)^T dO,  dP = (dO V^T) * Z,  D = rowsum(dO * O),
+ * dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *   Arguments as for fa_bwd plus p_drop, seed, offset as for fa_fwd_dropout
+ *   (o, m, l are what fa_fwd_dropout wrote).  Workspace:
+ *   fa_bwd_workspace_bytes(B, H, N, d) bytes.
+ */
+int fa_bwd_dropout(int B, int H, int N, int d, const void *q, const void *k,
+                   const void *v, const void *o, const void *dout,
+                   const float *m, const float *l, const int32_t *kv_len,
+                   int causal, float scale, float p_drop, uint64_t seed,
+                   uint32_t offset, void *dq, void *dk, void *dv,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * fa_fwd_block_sparse -- block-sparse attention (FA notes §4.4): the score
  * matrix is cut into 128 x 128 blocks and only the blocks the mask allows
  * are computed; masked blocks are skipped, not loaded.  Exact attention

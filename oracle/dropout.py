@@ -125,12 +125,15 @@ def dropout_keep(bh, rows, n_keys, seed, offset, threshold):
 
 
 def attention_fwd_dropout(q, k, v, p_drop, seed, offset=0, scale=None,
-                          causal=False, kv_len=None, row_chunk=512):
+                          causal=False, kv_len=None, rows=None,
+                          row_chunk=512):
     """Attention forward with dropout on P (FA notes §2.1 / §3.4), float64.
 
-    q, k, v: [B,H,N,d]; masking as in reference.attention_fwd.  Returns
-    (o, m, l): o = (P * Z * s) V with the mask Z of dropout_keep, and the
-    pre-dropout softmax statistics m, l.
+    q, k, v: [B,H,N,d]; masking as in reference.attention_fwd.  rows: None
+    for every query row, or the row indices to compute (a row's result
+    depends on that row alone).  Returns (o, m, l) over those rows:
+    o = (P * Z * s) V with the mask Z of dropout_keep, and the pre-dropout
+    softmax statistics m, l.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -138,20 +141,23 @@ def attention_fwd_dropout(q, k, v, p_drop, seed, offset=0, scale=None,
     B, H, N, d = q.shape
     sc = _default_scale(d, scale)
     T, ks = dropout_threshold(p_drop)
-    o = np.zeros((B, H, N, v.shape[3]))
-    m = np.full((B, H, N), -np.inf)
-    l = np.zeros((B, H, N))
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = rows.size
+    o = np.zeros((B, H, R, v.shape[3]))
+    m = np.full((B, H, R), -np.inf)
+    l = np.zeros((B, H, R))
     for b in range(B):
         valid = N if kv_len is None else int(kv_len[b])
-        for r0 in range(0, N, row_chunk):
-            rr = np.arange(r0, min(N, r0 + row_chunk))
+        for r0 in range(0, R, row_chunk):
+            rr = rows[r0:r0 + row_chunk]
+            out = slice(r0, r0 + rr.size)
             vis = visible_mask(rr, N, causal, valid)
             for h in range(H):
                 p, mm, ll = _row_softmax(sc * (q[b, h, rr] @ k[b, h].T), vis)
                 z = dropout_keep(b * H + h, rr, N, seed, offset, T)
-                o[b, h, rr] = (p * z * ks) @ v[b, h]
-                m[b, h, rr] = mm
-                l[b, h, rr] = ll
+                o[b, h, out] = (p * z * ks) @ v[b, h]
+                m[b, h, out] = mm
+                l[b, h, out] = ll
     return o, m, l
 
 

@@ -175,3 +175,28 @@ def test_block_sparse_validation(lib):
     assert bwd(mask=NULL) == -1
     assert bwd(ws=NULL) == -4
     assert bwd(ws_bytes=16) == -4
+
+
+def test_dropout_validation(lib):
+    def fwd(q=FAKE, N=64, d=64, p=0.1, m=NULL, scale=0.125):
+        return lib.fa_fwd_dropout(1, 2, N, d, q, FAKE, FAKE, FAKE, m, NULL,
+                                  NULL, 0, scale, p, 1, 0, NULL)
+    assert fwd(q=NULL) == -1
+    assert fwd(m=FAKE) == -1
+    assert fwd(N=0) == -2
+    assert fwd(scale=0.0) == -2
+    assert fwd(p=-0.01) == -2
+    assert fwd(p=float("nan")) == -2
+    assert fwd(p=255.5 / 256) == -2           # rounds to 256/256
+    assert fwd(p=1.0) == -2
+    assert fwd(d=96) == -3
+    assert fwd(d=96, p=0.5) == -3             # a valid p does not hide d
+
+    def bwd(ws=FAKE, ws_bytes=1 << 20, p=0.1, l=FAKE):
+        return lib.fa_bwd_dropout(1, 2, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, l, NULL, 1, 0.125, p, 7, 3, FAKE,
+                                  FAKE, FAKE, ws, ws_bytes, NULL)
+    assert bwd(l=NULL) == -1
+    assert bwd(p=2.0) == -2
+    assert bwd(ws=NULL) == -4
+    assert bwd(ws_bytes=16) == -4

@@ -234,3 +234,14 @@ def test_backward_finite_differences():
             pickm = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
             fd = (loss(*pick) - loss(*pickm)) / (2 * eps)
             assert abs(fd - g[idx]) <= 1e-7, (name, idx)
+
+
+def test_row_subset_equals_full_rows():
+    rng = np.random.default_rng(66)
+    q, k, v = (rng.standard_normal((1, 2, 70, 8)) for _ in range(3))
+    rows = np.array([69, 0, 33, 34])
+    o, m, l = attention_fwd_dropout(q, k, v, 0.3, 5, 1, None, True)
+    os_, ms, ls = attention_fwd_dropout(q, k, v, 0.3, 5, 1, None, True,
+                                        rows=rows)
+    assert np.array_equal(os_, o[:, :, rows])
+    assert np.array_equal(ms, m[:, :, rows]) and np.array_equal(ls, l[:, :, rows])

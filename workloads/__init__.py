@@ -151,6 +151,9 @@ class Workload:
     backward: bool = False
     # varlen only: sequence lengths ~ U{lo..hi}; N is the longest allowed
     seq_range: Optional[tuple] = None
+    # dense only: dropout on P with this drop probability (seed = the
+    # workload seed, offset 0)
+    p_drop: float = 0.0
     # decode only
     Hkv: int = 0
     ctx_range: Optional[tuple] = None
@@ -263,6 +266,11 @@ WORKLOADS = {
     "gpt2_medium_causal_4k": Workload(
         "gpt2_medium_causal_4k", 31, "attn", "bf16", 2, 16, 4096, 64,
         causal=True, qkv_mult=0.5, backward=True),
+    # The 4K GPT-2-medium step with attention dropout 0.1 (GPT-2's training
+    # setting for attention probabilities).
+    "gpt2_medium_causal_4k_dropout": Workload(
+        "gpt2_medium_causal_4k_dropout", 32, "attn", "bf16", 2, 16, 4096, 64,
+        causal=True, qkv_mult=0.5, backward=True, p_drop=0.1),
     "long_causal_16k_d128": Workload(
         "long_causal_16k_d128", 4, "attn", "bf16", 1, 16, 16384, 128,
         causal=True),
