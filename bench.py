@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -112,11 +113,18 @@ class Attn:
         from workloads import to_device
         self.w, self.fa, self.torch = w, fa, torch
         self.varlen = w.kind == "varlen"
+        self.fp8 = w.kind == "fp8"
         self.mask = None
         if w.kind == "sparse":
             from workloads import block_sparse_mask
             self.mask = torch.from_numpy(block_sparse_mask(w.H, w.N)).cuda()
-        if self.varlen:   # packed ragged batch, [H, total, d]
+        if self.fp8:      # E4M3 codes, V transposed, per-head descales
+            q, k, v, qd, kd, vd = w.fp8_inputs()
+            self.descales = [torch.from_numpy(x).cuda() for x in (qd, kd, vd)]
+            self.do = None
+            self.kv_len = None
+            nbytes = 1
+        elif self.varlen:   # packed ragged batch, [H, total, d]
             cu, q, k, v = w.varlen_inputs()
             self.cu = torch.from_numpy(cu).cuda()
             self.do = to_device(w.varlen_dout())
@@ -133,6 +141,9 @@ class Attn:
                               device="cuda")
 
     def fwd(self):
+        if self.fp8:
+            return self.fa.fwd_fp8(self.q, self.k, self.v, *self.descales,
+                                   causal=self.w.causal)
         if self.mask is not None:
             return self.fa.fwd_block_sparse(self.q, self.k, self.v, self.mask,
                                             causal=self.w.causal)
@@ -273,7 +284,8 @@ def sweep(steps, warmup):
     for name in ["bert_large_padded", "gpt2_medium_causal_1k",
                  "long_causal_16k_d128", "long_causal_64k_d64",
                  "varlen_causal_prefill", "block_sparse_16k",
-                 "gpt2_medium_causal_4k_dropout"]:
+                 "gpt2_medium_causal_4k_dropout",
+                 "long_causal_16k_d128_fp8"]:
         w = WORKLOADS[name]
         attn = Attn(w)
         step_ms, fwd_ms, bwd_ms, _ = time_step(attn, steps, warmup,
@@ -285,6 +297,12 @@ def sweep(steps, warmup):
             r["bwd_ms"] = round(bwd_ms, 4)
             r["bwd_tflops"] = round(w.bwd_flops() / bwd_ms / 1e9, 1)
             r["bwd_frac"] = round(r["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)
+        if w.kind == "fp8":   # against the bf16 forward of the same shape
+            r["fwd_frac_of_fp8_peak"] = round(r["fwd_tflops"] / PEAK_FP8_TFLOPS,
+                                              4)
+            bf = out.get("long_causal_16k_d128")
+            if bf is not None:
+                r["speedup_vs_bf16_fwd"] = round(bf["fwd_ms"] / fwd_ms, 2)
         if w.p_drop > 0:   # the same inputs without dropout
             import dataclasses
             plain = Attn(dataclasses.replace(w, p_drop=0.0))

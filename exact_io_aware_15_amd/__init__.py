@@ -19,7 +19,8 @@ import math
 
 from ._lib import FA_BF16, FA_F32, FaError, LibraryMissing, check, lib
 
-__all__ = ["fwd", "bwd", "fwd_dropout", "bwd_dropout", "fwd_varlen",
+__all__ = ["fwd", "bwd", "fwd_dropout", "bwd_dropout", "fwd_fp8",
+           "fwd_varlen",
            "bwd_varlen", "fwd_block_sparse",
            "bwd_block_sparse", "decode_paged",
            "prefill_paged",
@@ -94,6 +95,47 @@ def fwd(q, k, v, causal=False, kv_len=None, scale=None, return_stats=True):
                           _ptr(v), _ptr(o), _ptr(m), _ptr(l), _ptr(kv_len),
                           int(bool(causal)), scale, _stream(q))
     check("fa_fwd", st)
+    return o, m, l
+
+
+def fwd_fp8(q, k, v_t, q_descale=None, k_descale=None, v_descale=None,
+            causal=False, kv_len=None, scale=None, return_stats=True):
+    """Attention forward on FP8 (E4M3) operands.
+
+    q, k: [B,H,N,d] uint8 E4M3 codes; v_t: V transposed, [B,H,d,ldv] uint8
+    codes with ldv >= N a multiple of 16; descales: fp32 [B*H] (or [B,H])
+    tensors or None for 1.  The real inputs are code * descale.  Returns
+    (o, m, l): o bf16 [B,H,N,d], m, l fp32 [B,H,N] (None if not requested).
+    """
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check_dev("q", q, torch.uint8)
+    _check_dev("k", k, torch.uint8, q.shape)
+    _check_dev("v_t", v_t, torch.uint8)
+    if v_t.dim() != 4 or tuple(v_t.shape[:3]) != (B, H, d):
+        raise ValueError(f"v_t must be [B,H,d,ldv], got {tuple(v_t.shape)}")
+    ds = []
+    for name, t in (("q_descale", q_descale), ("k_descale", k_descale),
+                    ("v_descale", v_descale)):
+        if t is not None:
+            _check_dev(name, t, torch.float32)
+            if t.numel() != B * H:
+                raise ValueError(f"{name} must hold B*H values")
+        ds.append(t)
+    kv_len = _kv_len(kv_len, B, q.device)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+    m = l = None
+    if return_stats:
+        m = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        l = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib().fa_fwd_fp8(B, H, N, d, _ptr(q), _ptr(k), _ptr(v_t),
+                              v_t.shape[3], _ptr(ds[0]), _ptr(ds[1]),
+                              _ptr(ds[2]), _ptr(o), _ptr(m), _ptr(l),
+                              _ptr(kv_len), int(bool(causal)), scale,
+                              _stream(q))
+    check("fa_fwd_fp8", st)
     return o, m, l
 
 

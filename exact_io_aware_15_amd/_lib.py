@@ -23,6 +23,8 @@ SIGNATURES = {
     "fa_last_hip_error_str": (ctypes.c_char_p, []),
     "fa_fwd": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _F,
                     _P]),
+    "fa_fwd_fp8": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P,
+                        _P, _P, _I, _F, _P]),
     "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F,
                     _P, _P, _P, _P, _Z, _P]),

@@ -145,6 +145,28 @@ int fa_fwd_dropout(int B, int H, int N, int d, const void *q, const void *k,
                    scale, dr, stream);
 }
 
+int fa_fwd_fp8(int B, int H, int N, int d, const void *q, const void *k,
+               const void *v_t, int ldv, const float *q_descale,
+               const float *k_descale, const float *v_descale, void *o,
+               float *m, float *l, const int32_t *kv_len, int causal,
+               float scale, void *stream) {
+  if (!q || !k || !v_t || !o) return FA_E_NULLPTR;
+  if ((m == nullptr) != (l == nullptr)) return FA_E_NULLPTR;
+  if (!attn_shape_ok(B, H, N) || !valid_scale(scale)) return FA_E_SHAPE;
+  if (ldv < N || ldv % 16 != 0) return FA_E_SHAPE;
+  if ((long long)B * H * ldv > (1LL << 40)) return FA_E_SHAPE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v_t) % 16) return FA_E_SHAPE;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  Fp8FwdArgs a{};
+  a.q = (const uint8_t *)q; a.k = (const uint8_t *)k;
+  a.vt = (const uint8_t *)v_t; a.ldv = ldv;
+  a.q_descale = q_descale; a.k_descale = k_descale; a.v_descale = v_descale;
+  a.o = (uint16_t *)o; a.m = m; a.l = l; a.kv_len = kv_len;
+  a.B = B; a.H = H; a.N = N; a.BH = B * H;
+  a.scale = scale;
+  return from_hip(launch_fwd_fp8(a, d, causal != 0, (hipStream_t)stream));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (!attn_shape_ok(B, H, N) || (d != 64 && d != 128)) return 0;
   const size_t rows = (size_t)B * H * N;

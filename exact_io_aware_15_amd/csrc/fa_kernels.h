@@ -50,6 +50,22 @@ hipError_t launch_fwd_block_sparse(const FwdArgs &a, int d, bool causal,
 hipError_t launch_fwd_f32(const FwdArgs &a, int d, bool causal,
                           hipStream_t s);
 
+// FP8 forward: Q, K [B,H,N,d] and V^T [B,H,d,ldv] as E4M3 codes with
+// per-(batch, head) fp32 descales (null = 1); O bf16 [B,H,N,d].
+struct Fp8FwdArgs {
+  const uint8_t *q, *k, *vt;
+  int ldv;                 // V^T row stride in bytes, >= N, multiple of 16
+  const float *q_descale, *k_descale, *v_descale;  // [B*H] or null
+  uint16_t *o;
+  float *m, *l;            // [B,H,N] or both null
+  const int32_t *kv_len;   // [B] or null
+  int B, H, N, BH;
+  float scale;
+};
+
+hipError_t launch_fwd_fp8(const Fp8FwdArgs &a, int d, bool causal,
+                          hipStream_t s);
+
 struct BwdArgs {
   const uint16_t *q, *k, *v, *o, *dout;  // [B,H,N,d] or [H,total,d] bf16
   const float *m, *l;                    // [B,H,N] or [H,total]

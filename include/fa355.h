@@ -91,6 +91,39 @@ int fa_fwd(int dtype, int B, int H, int N, int d,
            void *stream);
 
 /*
+ * fa_fwd_fp8 -- the forward of fa_fwd with FP8 operands.  The pages name FP8
+ * support only as a FlashAttention-3 feature (S12, production-practice list)
+ * and give no scaling convention; this entry point takes E4M3
+ * codes (OCP "E4M3FN": bias 7, no infinities, max 448) with one fp32
+ * descale per (batch, head) and tensor: the real inputs are code * descale.
+ * Both products run on the FP8 matrix instructions.  The probabilities are
+ * rounded to E4M3 before the P V product (after a 2^6 shift that keeps
+ * them inside the format's range), so O carries a relative error of up to
+ * 2^-4 per probability on top of the input quantisation; m and l are
+ * computed in fp32 from the unrounded probabilities.
+ *
+ *   B, H, N, d, kv_len, causal, scale, stream   as for fa_fwd.
+ *   q, k         [B,H,N,d] E4M3 codes (uint8), 16-byte aligned.
+ *   v_t          V transposed: [B,H,d,ldv] E4M3 codes, 16-byte aligned
+ *                (V's key axis is the contraction axis of P V, so it is the
+ *                contiguous one; a quantisation pass can write it so).
+ *                Columns >= N (and >= kv_len[b]) are ignored.
+ *   ldv          row stride of v_t in bytes: >= N and a multiple of 16.
+ *   q_descale,
+ *   k_descale,
+ *   v_descale    device fp32 [B*H] (index b*H + h), finite and > 0, or
+ *                NULL for 1.
+ *   o            [B,H,N,d] bf16, written.
+ *   m, l         [B,H,N] fp32 as for fa_fwd (statistics of the scaled
+ *                scores of the dequantised inputs), or both NULL.
+ */
+int fa_fwd_fp8(int B, int H, int N, int d, const void *q, const void *k,
+               const void *v_t, int ldv, const float *q_descale,
+               const float *k_descale, const float *v_descale, void *o,
+               float *m, float *l, const int32_t *kv_len, int causal,
+               float scale, void *stream);
+
+/*
  * fa_bwd_workspace_bytes -- device workspace fa_bwd needs for this shape: two
  * fp32 row vectors [B,H,N] (D = rowsum(dO * O) and the log2-domain row
  * offset m*log2(e) + log2(l)), each padded to 256 bytes.  Returns 0 for

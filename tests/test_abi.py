@@ -21,7 +21,7 @@ NULL = None
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -200,3 +200,18 @@ def test_dropout_validation(lib):
     assert bwd(p=2.0) == -2
     assert bwd(ws=NULL) == -4
     assert bwd(ws_bytes=16) == -4
+
+
+def test_fp8_validation(lib):
+    def call(q=FAKE, vt=FAKE, N=100, ldv=112, d=128, m=NULL, scale=0.1):
+        return lib.fa_fwd_fp8(1, 2, N, d, q, FAKE, vt, ldv, NULL, NULL, NULL,
+                              FAKE, m, NULL, NULL, 1, scale, NULL)
+    assert call(q=NULL) == -1
+    assert call(vt=NULL) == -1
+    assert call(m=FAKE) == -1
+    assert call(N=0) == -2
+    assert call(ldv=96) == -2                 # < N
+    assert call(ldv=104) == -2                # not a multiple of 16
+    assert call(vt=ctypes.c_void_p(0x1008)) == -2   # not 16-byte aligned
+    assert call(scale=-1.0) == -2
+    assert call(d=96) == -3

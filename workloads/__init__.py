@@ -42,9 +42,41 @@ def bf16_value(bits):
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
+def e4m3_value(codes):
+    """uint8 FP8 E4M3 codes (OCP "E4M3FN": 1 sign bit, 4 exponent bits with
+    bias 7, 3 mantissa bits; no infinities; S.1111.111 is NaN) -> float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    mant = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, mant / 8.0 * 2.0 ** -6,
+                   (1.0 + mant / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
+_E4M3_POS = e4m3_value(np.arange(0x7F, dtype=np.uint8))   # 0 .. 448, ascending
+E4M3_MAX = float(_E4M3_POS[-1])
+
+
+def e4m3_codes(x):
+    """float array -> uint8 E4M3 codes: nearest value, ties to the even code
+    (even mantissa), magnitudes beyond 448 saturated to 448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a), 1, 0x7E)
+    lo = hi - 1
+    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi,
+                                            np.where(lo % 2 == 0, lo, hi)))
+    return (pick | np.where(x < 0, 0x80, 0)).astype(np.uint8)
+
+
 def to_device(t, device="cuda"):
     """Copy a generated Tensor to a torch GPU tensor with the same bits."""
     import torch
+    if t.dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(t.store)).to(device)
     if t.dtype == "bf16":
         x = torch.from_numpy(np.ascontiguousarray(t.store).view(np.int16))
         return x.view(torch.bfloat16).to(device)
@@ -54,8 +86,8 @@ def to_device(t, device="cuda"):
 @dataclass
 class Tensor:
     """A generated tensor: storage bits (bf16) or fp32 data, plus exact fp64."""
-    dtype: str            # "bf16" or "f32"
-    store: np.ndarray     # uint16 bits for bf16, float32 for f32
+    dtype: str            # "bf16", "f32" or "fp8"
+    store: np.ndarray     # uint16 bits (bf16), float32 (f32), uint8 E4M3 (fp8)
     exact: np.ndarray     # float64 copy of the stored values
 
     @property
@@ -74,6 +106,31 @@ def normal(shape, cfg_seed, tensor_id, dtype, mult=1.0):
     if dtype == "f32":
         return Tensor("f32", x, x.astype(np.float64))
     raise ValueError(dtype)
+
+
+def normal_fp8(shape, cfg_seed, tensor_id, mult=1.0, transpose=False):
+    """iid N(0,1) * mult drawn in fp32 (as ``normal``) and quantized to FP8
+    E4M3 per (batch, head): descale = amax / 448 (fp32), codes =
+    E4M3(x / descale).  Returns (Tensor, descale float32 [B*H]).  The
+    Tensor's ``exact`` is codes * descale in float64 with the logical
+    [B,H,N,d] shape; with transpose=True its ``store`` is [B,H,d,ldv], the
+    key axis last and padded with zero codes to ldv = N rounded up to 16.
+    """
+    B, H, N, d = shape
+    x = rng(cfg_seed, tensor_id).standard_normal(size=shape, dtype=np.float32)
+    if mult != 1.0:
+        x = (x * np.float32(mult)).astype(np.float32)
+    amax = np.abs(x).reshape(B * H, -1).max(axis=1).astype(np.float64)
+    descale = np.maximum(amax / E4M3_MAX, 2.0 ** -100).astype(np.float32)
+    ds = descale.astype(np.float64).reshape(B, H, 1, 1)
+    codes = e4m3_codes(x.astype(np.float64) / ds)
+    exact = e4m3_value(codes) * ds
+    store = codes
+    if transpose:
+        ldv = -(-N // 16) * 16
+        store = np.zeros((B, H, d, ldv), np.uint8)
+        store[..., :N] = np.swapaxes(codes, 2, 3)
+    return Tensor("fp8", store, exact), descale
 
 
 def uniform_int(n, lo, hi, cfg_seed, tensor_id):
@@ -165,6 +222,16 @@ class Workload:
         shape = (self.B, self.H, self.N, self.d)
         return tuple(normal(shape, self.seed, t, self.dtype, self.qkv_mult)
                      for t in (TID_Q, TID_K, TID_V))
+
+    def fp8_inputs(self):
+        """(q, k, v_t, q_descale, k_descale, v_descale) for an FP8 forward:
+        Q and K [B,H,N,d] E4M3, V transposed [B,H,d,ldv] (see normal_fp8)."""
+        shape = (self.B, self.H, self.N, self.d)
+        q, qd = normal_fp8(shape, self.seed, TID_Q, self.qkv_mult)
+        k, kd = normal_fp8(shape, self.seed, TID_K, self.qkv_mult)
+        v, vd = normal_fp8(shape, self.seed, TID_V, self.qkv_mult,
+                           transpose=True)
+        return q, k, v, qd, kd, vd
 
     def dout(self):
         return normal((self.B, self.H, self.N, self.d), self.seed, TID_DO,
@@ -289,6 +356,10 @@ WORKLOADS = {
     "block_sparse_16k": Workload(
         "block_sparse_16k", 8, "sparse", "bf16", 1, 16, 16384, 64,
         qkv_mult=0.5, backward=True),
+    # FP8 (E4M3) forward on the 16K causal d = 128 shape, per-head scales.
+    "long_causal_16k_d128_fp8": Workload(
+        "long_causal_16k_d128_fp8", 9, "fp8", "fp8", 1, 16, 16384, 128,
+        causal=True),
     "long_causal_64k_d64": Workload(
         "long_causal_64k_d64", 41, "attn", "bf16", 1, 2, 65536, 64,
         causal=True),
