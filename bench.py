@@ -95,6 +95,9 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the paged decode (paged_gqa_decode)")
+    ap.add_argument("--sweep-only", default=None, metavar="WORKLOAD",
+                    help="time only this sweep workload (or "
+                         "paged_chunked_prefill) and print its entry")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -278,51 +281,58 @@ def prefill_bench(steps, warmup):
             "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
-def sweep(steps, warmup):
+SWEEP = ["bert_large_padded", "gpt2_medium_causal_1k", "long_causal_16k_d128",
+         "long_causal_64k_d64", "varlen_causal_prefill", "block_sparse_16k",
+         "gpt2_medium_causal_4k_dropout", "long_causal_16k_d128_fp8"]
+
+
+def sweep_one(name, steps, warmup, out):
+    """Times one sweep workload (forward, and backward where it has one);
+    comparisons refer to entries already in `out`."""
+    import dataclasses
     from workloads import WORKLOADS
+    w = WORKLOADS[name]
+    attn = Attn(w)
+    step_ms, fwd_ms, bwd_ms, _ = time_step(attn, steps, warmup,
+                                           backward=w.backward)
+    r = {"fwd_ms": round(fwd_ms, 4),
+         "fwd_tflops": round(w.fwd_flops() / fwd_ms / 1e9, 1)}
+    r["fwd_frac"] = round(r["fwd_tflops"] / PEAK_BF16_TFLOPS, 4)
+    if w.backward:
+        r["bwd_ms"] = round(bwd_ms, 4)
+        r["bwd_tflops"] = round(w.bwd_flops() / bwd_ms / 1e9, 1)
+        r["bwd_frac"] = round(r["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)
+    if w.kind == "fp8":   # against the bf16 forward of the same shape
+        r["fwd_frac_of_fp8_peak"] = round(r["fwd_tflops"] / PEAK_FP8_TFLOPS,
+                                          4)
+        bf = out.get("long_causal_16k_d128")
+        if bf is not None:
+            r["speedup_vs_bf16_fwd"] = round(bf["fwd_ms"] / fwd_ms, 2)
+    if w.p_drop > 0:   # the same inputs without dropout
+        plain = Attn(dataclasses.replace(w, p_drop=0.0))
+        _, pfwd, pbwd, _ = time_step(plain, steps, warmup, backward=True)
+        r["no_dropout_fwd_ms"] = round(pfwd, 4)
+        r["no_dropout_bwd_ms"] = round(pbwd, 4)
+        r["dropout_cost_fwd"] = round(fwd_ms / pfwd, 3)
+        r["dropout_cost_bwd"] = round(bwd_ms / pbwd, 3)
+        del plain
+    if w.kind == "sparse":   # the same shape without the mask
+        dense = Attn(dataclasses.replace(w, kind="attn"))
+        _, dfwd, dbwd, _ = time_step(dense, steps, warmup, backward=True)
+        r["dense_fwd_ms"] = round(dfwd, 4)
+        r["dense_bwd_ms"] = round(dbwd, 4)
+        r["speedup_fwd"] = round(dfwd / fwd_ms, 2)
+        r["speedup_bwd"] = round(dbwd / bwd_ms, 2)
+        del dense
+    out[name] = r
+    del attn
+    return r
+
+
+def sweep(steps, warmup):
     out = {}
-    for name in ["bert_large_padded", "gpt2_medium_causal_1k",
-                 "long_causal_16k_d128", "long_causal_64k_d64",
-                 "varlen_causal_prefill", "block_sparse_16k",
-                 "gpt2_medium_causal_4k_dropout",
-                 "long_causal_16k_d128_fp8"]:
-        w = WORKLOADS[name]
-        attn = Attn(w)
-        step_ms, fwd_ms, bwd_ms, _ = time_step(attn, steps, warmup,
-                                               backward=w.backward)
-        r = {"fwd_ms": round(fwd_ms, 4),
-             "fwd_tflops": round(w.fwd_flops() / fwd_ms / 1e9, 1)}
-        r["fwd_frac"] = round(r["fwd_tflops"] / PEAK_BF16_TFLOPS, 4)
-        if w.backward:
-            r["bwd_ms"] = round(bwd_ms, 4)
-            r["bwd_tflops"] = round(w.bwd_flops() / bwd_ms / 1e9, 1)
-            r["bwd_frac"] = round(r["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)
-        if w.kind == "fp8":   # against the bf16 forward of the same shape
-            r["fwd_frac_of_fp8_peak"] = round(r["fwd_tflops"] / PEAK_FP8_TFLOPS,
-                                              4)
-            bf = out.get("long_causal_16k_d128")
-            if bf is not None:
-                r["speedup_vs_bf16_fwd"] = round(bf["fwd_ms"] / fwd_ms, 2)
-        if w.p_drop > 0:   # the same inputs without dropout
-            import dataclasses
-            plain = Attn(dataclasses.replace(w, p_drop=0.0))
-            _, pfwd, pbwd, _ = time_step(plain, steps, warmup, backward=True)
-            r["no_dropout_fwd_ms"] = round(pfwd, 4)
-            r["no_dropout_bwd_ms"] = round(pbwd, 4)
-            r["dropout_cost_fwd"] = round(fwd_ms / pfwd, 3)
-            r["dropout_cost_bwd"] = round(bwd_ms / pbwd, 3)
-            del plain
-        if w.kind == "sparse":   # the same shape without the mask
-            import dataclasses
-            dense = Attn(dataclasses.replace(w, kind="attn"))
-            _, dfwd, dbwd, _ = time_step(dense, steps, warmup, backward=True)
-            r["dense_fwd_ms"] = round(dfwd, 4)
-            r["dense_bwd_ms"] = round(dbwd, 4)
-            r["speedup_fwd"] = round(dfwd / fwd_ms, 2)
-            r["speedup_bwd"] = round(dbwd / bwd_ms, 2)
-            del dense
-        out[name] = r
-        del attn
+    for name in SWEEP:
+        sweep_one(name, steps, warmup, out)
     out["paged_gqa_decode"] = decode_bench(max(steps, 20), warmup)
     out["paged_chunked_prefill"] = prefill_bench(max(steps, 20), warmup)
     return out
@@ -400,6 +410,13 @@ def main():
         return
     if args.decode_only:
         print(json.dumps(decode_bench(args.steps, args.warmup)), flush=True)
+        return
+    if args.sweep_only:
+        if args.sweep_only == "paged_chunked_prefill":
+            r = prefill_bench(args.steps, args.warmup)
+        else:
+            r = sweep_one(args.sweep_only, args.steps, args.warmup, {})
+        print(json.dumps({args.sweep_only: r}), flush=True)
         return
     w = WORKLOADS[args.workload]
     attn = Attn(w)
