@@ -25,8 +25,6 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # fp32 arithmetic stays unpacked (v_pk_*_f32 forms are avoided)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # hardware fp32 atomic add for the dQ accumulator
-    "-munsafe-fp-atomics",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
