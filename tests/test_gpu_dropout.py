@@ -128,6 +128,8 @@ CASES = [  # (B, H, N, d, causal, kv_len, p)
     (2, 2, 384, 128, True, [384, 200], 0.5),
     (2, 2, 250, 128, False, [250, 0], 0.1),
     (1, 1, 77, 64, True, [60], 0.5),
+    (1, 2, 1, 64, False, None, 0.5),      # one query, one key
+    (1, 1, 17, 128, True, None, 0.3),     # shorter than one tile
 ]
 
 

@@ -82,6 +82,7 @@ EXACT = [  # (B, H, N, d, causal, kv_len)
     (1, 3, 256, 128, False, [256]),
     (2, 1, 190, 128, True, [190, 77]),
     (1, 1, 64, 128, False, [0]),
+    (1, 2, 1, 64, True, None),            # one query, one key
 ]
 
 
@@ -144,6 +145,7 @@ RANDOM = [  # (B, H, N, d, causal, kv_len)
     (1, 3, 517, 64, True, None),
     (2, 2, 384, 128, True, [384, 130]),
     (1, 2, 250, 128, False, [200]),
+    (2, 1, 17, 128, True, None),          # shorter than one tile
 ]
 
 
