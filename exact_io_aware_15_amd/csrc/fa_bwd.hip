@@ -158,12 +158,24 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   }
   auto next_step = [&](int st) { return SPARSE ? walk.next(st) : st; };
 
+  // Q / dO step fills: uniform-base DMA for whole steps, the clamped
+  // (out-of-line) fill for the ragged last one.
+  const DmaOffsets<D, BR> doff;
+  auto load_step = [&](int q1, int b2) {
+    if (q1 + BR <= N) {
+      dma_tile_at<D, BR>(Qs[b2], qg + (size_t)q1 * D, doff);
+      dma_tile_at<D, BR>(dOs[b2], dog + (size_t)q1 * D, doff);
+    } else {
+      dma_tile_tail<D, BR>(Qs[b2], qg, q1, N - 1);
+      dma_tile_tail<D, BR>(dOs[b2], dog, q1, N - 1);
+    }
+  };
+
   float l_nx = 0.f, d_nx = 0.f;
   int st = next_step(q_begin / BR);
   if (st < nsteps) {
     const int q1 = st * BR;
-    dma_tile<D, BR>(Qs[0], qg, q1, N - 1);
-    dma_tile<D, BR>(dOs[0], dog, q1, N - 1);
+    load_step(q1, 0);
     if (tid < BR) {
       load_stats(q1, l_nx, d_nx);
       LDs[0][2 * tid] = l_nx;
@@ -178,8 +190,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const int sn = next_step(st + 1);
     const bool has_next = sn < nsteps;
     if (has_next) {  // the other buffers were last read before the barrier
-      dma_tile<D, BR>(Qs[buf ^ 1], qg, sn * BR, N - 1);
-      dma_tile<D, BR>(dOs[buf ^ 1], dog, sn * BR, N - 1);
+      load_step(sn * BR, buf ^ 1);
       if (tid < BR) load_stats(sn * BR, l_nx, d_nx);
     }
     const uint16_t *Qt = Qs[buf];
@@ -364,20 +375,27 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
   }
   auto next_tile = [&](int t) { return SPARSE ? walk.next(t) : t; };
 
+  // K / V tile fills: uniform-base DMA for whole tiles, the clamped
+  // (out-of-line) fill for the tail.
+  const DmaOffsets<D, BC> doff;
+  auto load_tile = [&](int k0, int b2) {
+    if (k0 + BC <= kv_valid) {
+      dma_tile_at<D, BC>(Ks[b2], kg + (size_t)k0 * D, doff);
+      dma_tile_at<D, BC>(Vs[b2], vg + (size_t)k0 * D, doff);
+    } else {
+      dma_tile_tail<D, BC>(Ks[b2], kg, k0, kv_valid - 1);
+      dma_tile_tail<D, BC>(Vs[b2], vg, k0, kv_valid - 1);
+    }
+  };
   int t = next_tile(0);
-  if (t < ntiles) {
-    dma_tile<D, BC>(Ks[0], kg, t * BC, kv_valid - 1);
-    dma_tile<D, BC>(Vs[0], vg, t * BC, kv_valid - 1);
-  }
+  if (t < ntiles) load_tile(t * BC, 0);
   wait_dma();
   __syncthreads();
   for (int buf = 0; t < ntiles; buf ^= 1) {
     const int k0 = t * BC;
     const int tn = next_tile(t + 1);
-    if (tn < ntiles) {  // the other buffer was last read before the barrier
-      dma_tile<D, BC>(Ks[buf ^ 1], kg, tn * BC, kv_valid - 1);
-      dma_tile<D, BC>(Vs[buf ^ 1], vg, tn * BC, kv_valid - 1);
-    }
+    if (tn < ntiles)  // the other buffer was last read before the barrier
+      load_tile(tn * BC, buf ^ 1);
     const uint16_t *Kt = Ks[buf];
     const uint16_t *Vt = Vs[buf];
     if (!(CAUSAL && k0 > qw + 31)) {  // else: tile above the diagonal

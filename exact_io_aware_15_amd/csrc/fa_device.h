@@ -324,6 +324,56 @@ __device__ __forceinline__ void dma_tile(uint16_t *tile, const uint16_t *src,
   }
 }
 
+// Per-lane byte offsets of dma_tile's sources relative to the tile's first
+// row: they depend only on the lane and the segment, so a kernel computes
+// them once and every tile that lies wholly inside the valid rows is filled
+// by dma_tile_at with a uniform base address (no per-tile address arithmetic).
+template <int W, int ROWS>
+struct DmaOffsets {
+  static constexpr int SEGS = ROWS * W * 2 / 1024;
+  uint32_t off[SEGS / 4];
+  __device__ __forceinline__ DmaOffsets() {
+    constexpr int CPR = W / 8;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int u = 0; u < SEGS / 4; ++u) {
+      const int p = (wave + 4 * u) * 64 + lane;
+      const int r = p / CPR, phys = p % CPR;
+      const int row = (r & ~31) | row_perm(r & 31);
+      off[u] = (uint32_t)((row * W + (phys ^ lds_swz<W>(r)) * 8) * 2);
+    }
+  }
+};
+
+// dma_tile for rows row0 .. row0+ROWS-1 all valid: src_rows points at row
+// row0 (a wave-uniform address), o holds the per-lane offsets.
+template <int W, int ROWS>
+__device__ __forceinline__ void dma_tile_at(uint16_t *tile,
+                                            const uint16_t *src_rows,
+                                            const DmaOffsets<W, ROWS> &o) {
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < DmaOffsets<W, ROWS>::SEGS / 4; ++u) {
+    const int seg = wave + 4 * u;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void *)(
+            (const char *)src_rows + o.off[u]),
+        (__attribute__((address_space(3))) void *)(tile + seg * 512), 16, 0,
+        0);
+  }
+}
+
+// dma_tile kept out of line, for the rare tail tile of a loop whose other
+// tiles use dma_tile_at (its address arithmetic then stays out of the loop's
+// register budget).
+template <int W, int ROWS>
+__device__ __attribute__((noinline)) void dma_tile_tail(uint16_t *tile,
+                                                        const uint16_t *src,
+                                                        int row0,
+                                                        int last_row) {
+  dma_tile<W, ROWS>(tile, src, row0, last_row);
+}
+
 // The same fill for a 64-row key or value tile of a paged cache: logical
 // row t of the tile is token t % 16 of cache block blk[t / 16], whose 16 x W
 // tile for this KV head starts at base + blk * blk_stride (base already

@@ -124,13 +124,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     }
   };
   int e_next[4] = {0, 0, 0, 0};
+  const DmaOffsets<D, BC> doff;
   auto load_tile = [&](int k0, int buf) {
     if (PAGED) {
       dma_tile_paged<D>(Ks[buf], kg, blk_stride, e_next, k0, kv_valid - 1);
       dma_tile_paged<D>(Vs[buf], vg, blk_stride, e_next, k0, kv_valid - 1);
+    } else if (k0 + BC <= kv_valid) {  // whole tile valid: uniform base
+      dma_tile_at<D, BC>(Ks[buf], kg + (size_t)k0 * D, doff);
+      dma_tile_at<D, BC>(Vs[buf], vg + (size_t)k0 * D, doff);
     } else {
-      dma_tile<D, BC>(Ks[buf], kg, k0, kv_valid - 1);
-      dma_tile<D, BC>(Vs[buf], vg, k0, kv_valid - 1);
+      dma_tile_tail<D, BC>(Ks[buf], kg, k0, kv_valid - 1);
+      dma_tile_tail<D, BC>(Vs[buf], vg, k0, kv_valid - 1);
     }
   };
 
