@@ -79,6 +79,33 @@ __device__ __forceinline__ u32x4 keep_bytes(u32x4 x, int n) {
   return x;
 }
 
+// Clamped fill of a tile that reaches past the valid keys or past ldv (kept
+// out of line: it runs at most once per workgroup).
+template <int D>
+__device__ __attribute__((noinline)) void fp8_tail_tile(
+    uint8_t *ks, uint8_t *vs, const uint8_t *kg, const uint8_t *vtg, int k0,
+    int kv_valid, int ldv) {
+  constexpr int KCH = D / 16;
+  constexpr int SEGS = 64 * D / 1024;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int u = 0; u < SEGS / 4; ++u) {
+    const int seg = wave + 4 * u;
+    const int p = seg * 64 + lane;
+    const int r = p / KCH, phys = p % KCH;
+    const int key = min(k0 + key_perm8(r), kv_valid - 1);
+    dma16(kg + (size_t)key * D + (phys ^ k_swz<D>(r)) * 16, ks + seg * 1024);
+  }
+#pragma unroll
+  for (int u = 0; u < SEGS / 4; ++u) {
+    const int seg = wave + 4 * u;
+    const int p = seg * 64 + lane;
+    const int r = p >> 2, phys = p & 3;
+    const int kc = min(k0 + 16 * (phys ^ vt_swz(r)), ldv - 16);
+    dma16(vtg + (size_t)r * ldv + kc, vs + seg * 1024);
+  }
+}
+
 template <int D, bool CAUSAL, bool PADDED>
 __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8FwdArgs a) {
   constexpr int BR = 128;        // queries per workgroup
@@ -146,24 +173,29 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8FwdArgs a) {
   // valid key), chunks permuted by k_swz.  V^T tile: row = head dimension,
   // 64 key bytes, chunks permuted by vt_swz; chunks starting at or past ldv
   // read the row's last chunk instead (its keys are masked).
+  // Per-lane source offsets of a whole tile (relative to its first key),
+  // computed once: tiles inside the valid keys are fetched from a uniform
+  // base; the tail tile takes the clamped path.
+  uint32_t koff[SEGS / 4], voff[SEGS / 4];
+#pragma unroll
+  for (int u = 0; u < SEGS / 4; ++u) {
+    const int p = (wave + 4 * u) * 64 + lane;
+    const int rk = p / KCH, pk = p % KCH;
+    koff[u] = (uint32_t)(key_perm8(rk) * D + (pk ^ k_swz<D>(rk)) * 16);
+    const int rv = p >> 2, pv = p & 3;
+    voff[u] = (uint32_t)(rv * ldv + 16 * (pv ^ vt_swz(rv)));
+  }
   auto load_tile = [&](int k0, int buf) {
+    if (k0 + BC <= kv_valid && k0 + BC <= ldv) {
 #pragma unroll
-    for (int u = 0; u < SEGS / 4; ++u) {
-      const int seg = wave + 4 * u;
-      const int p = seg * 64 + lane;
-      const int r = p / KCH, phys = p % KCH;
-      const int key = min(k0 + key_perm8(r), kv_valid - 1);
-      dma16(kg + (size_t)key * D + (phys ^ k_swz<D>(r)) * 16,
-            Ks(buf) + seg * 1024);
+      for (int u = 0; u < SEGS / 4; ++u) {
+        const int seg = wave + 4 * u;
+        dma16(kg + (size_t)k0 * D + koff[u], Ks(buf) + seg * 1024);
+        dma16(vtg + k0 + voff[u], Vs(buf) + seg * 1024);
+      }
+      return;
     }
-#pragma unroll
-    for (int u = 0; u < SEGS / 4; ++u) {
-      const int seg = wave + 4 * u;
-      const int p = seg * 64 + lane;
-      const int r = p >> 2, phys = p & 3;
-      const int kc = min(k0 + 16 * (phys ^ vt_swz(r)), ldv - 16);
-      dma16(vtg + (size_t)r * ldv + kc, Vs(buf) + seg * 1024);
-    }
+    fp8_tail_tile<D>(Ks(buf), Vs(buf), kg, vtg, k0, kv_valid, ldv);
   };
 
   if (ntiles > 0) load_tile(0, 0);
