@@ -13,6 +13,8 @@
 // fa_device.h); exponentials are taken as exp2 with scale*log2(e) folded into
 // one FMA; p is rounded to bf16 once and that same value feeds both the P V
 // MFMA and the row sum.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -159,7 +161,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
   wait_dma();
   __syncthreads();
-  for (int buf = 0; t < ntiles; buf ^= 1) {
+  // One tile; the loop below instantiates it for buffer 0 and buffer 1 so
+  // that every LDS address is a per-lane base plus a constant offset.
+  auto step = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int k0 = t * BC;
     const int tn = next_tile(t + 1);
     // The other buffer was last read before the previous barrier.
@@ -283,6 +288,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
     wait_dma();  // the next tile has landed
     __syncthreads();
     t = tn;
+  };
+  while (t < ntiles) {
+    step(std::integral_constant<int, 0>{});
+    if (t >= ntiles) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   // Epilogue: O = o / l (0 for a row with no visible key); m in natural
