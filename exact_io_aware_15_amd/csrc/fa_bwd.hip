@@ -185,7 +185,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   wait_dma();
   __syncthreads();
 
-  for (int buf = 0; st < nsteps; buf ^= 1) {
+  // One step; instantiated for buffer 0 and buffer 1 so that every LDS
+  // address is a per-lane base plus a constant offset.
+  auto step = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int q0 = st * BR;
     const int sn = next_step(st + 1);
     const bool has_next = sn < nsteps;
@@ -283,6 +286,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     wait_dma();
     __syncthreads();
     st = sn;
+  };
+  while (st < nsteps) {
+    step(std::integral_constant<int, 0>{});
+    if (st >= nsteps) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   // Epilogue: dK = scale * dK_acc, dV (times the dropout keep scale);
@@ -391,7 +399,9 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
   if (t < ntiles) load_tile(t * BC, 0);
   wait_dma();
   __syncthreads();
-  for (int buf = 0; t < ntiles; buf ^= 1) {
+  // One tile, instantiated per buffer (see bwd_dkdv_kernel).
+  auto step = [&](auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int k0 = t * BC;
     const int tn = next_tile(t + 1);
     if (tn < ntiles)  // the other buffer was last read before the barrier
@@ -468,6 +478,11 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
     wait_dma();  // the next tile has landed
     __syncthreads();
     t = tn;
+  };
+  while (t < ntiles) {
+    step(std::integral_constant<int, 0>{});
+    if (t >= ntiles) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   if (qi < N) {
