@@ -184,10 +184,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+      // ks outer: the two key blocks' accumulations alternate, so each
+      // MFMA's predecessor in the pipe is independent of it.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
+        for (int kb = 0; kb < 2; ++kb) {
           const bf16x8 kf = lds_row_frag<D>(Kt, kb * 32 + ln, ks * 16 + 8 * hh);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
