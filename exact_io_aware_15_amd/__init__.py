@@ -13,8 +13,10 @@ the library is missing, the calls raise.
     out = decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits=8)
     o, m, l = prefill_paged(q, k_cache, v_cache, block_table, seq_lens,
                             cu_seqlens_q, max_q, causal=True)
+    bits = debug_flags(clear=False)     # debug build (FA355_DEBUG=1) only
 """
 
+import ctypes
 import math
 
 from ._lib import FA_BF16, FA_F32, FaError, LibraryMissing, check, lib
@@ -25,7 +27,22 @@ __all__ = ["fwd", "bwd", "fwd_dropout", "bwd_dropout", "fwd_fp8",
            "bwd_block_sparse", "decode_paged",
            "prefill_paged",
            "bwd_workspace_bytes", "bwd_varlen_workspace_bytes",
-           "decode_workspace_bytes", "FaError", "LibraryMissing"]
+           "decode_workspace_bytes", "debug_flags", "CHECK_KV_LEN",
+           "CHECK_CU_SEQLENS", "CHECK_SEQ_LENS", "CHECK_BLOCK_TABLE",
+           "FaError", "LibraryMissing"]
+
+# Bits of the debug build's contract word (FA_CHECK_* in fa355.h).
+CHECK_KV_LEN, CHECK_CU_SEQLENS, CHECK_SEQ_LENS, CHECK_BLOCK_TABLE = 1, 2, 4, 8
+
+
+def debug_flags(clear=False):
+    """The debug build's record of contract violations on the current device
+    (an OR of CHECK_* bits since the last clear); waits for the device.
+    Raises FaError (FA_E_UNSUPPORTED) when the ordinary build is loaded."""
+    word = ctypes.c_uint32(0)
+    check("fa_debug_flags", lib().fa_debug_flags(ctypes.byref(word),
+                                                 int(bool(clear))))
+    return word.value
 
 
 def _torch():

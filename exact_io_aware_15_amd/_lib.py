@@ -1,14 +1,20 @@
 """ctypes loader for libfa355.so (the C ABI declared in include/fa355.h).
 
 The library is required: if it has not been built, every entry point raises
-instead of falling back to any other implementation.
+instead of falling back to any other implementation.  With FA355_DEBUG set in
+the environment (to anything but "" or "0") the debug build,
+libfa355_debug.so, is loaded instead: the same kernels, preceded by checks of
+the callers' device arrays (see debug_flags in the package).
 """
 
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                        "libfa355.so")
+_HERE = os.path.dirname(os.path.abspath(__file__))
+RELEASE_LIB_PATH = os.path.join(_HERE, "libfa355.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libfa355_debug.so")
+LIB_PATH = (DEBUG_LIB_PATH if os.environ.get("FA355_DEBUG", "0") not in
+            ("", "0") else RELEASE_LIB_PATH)
 
 FA_F32, FA_BF16 = 0, 1
 STATUS = {0: "FA_OK", -1: "FA_E_NULLPTR", -2: "FA_E_SHAPE",
@@ -21,6 +27,7 @@ SIGNATURES = {
     "fa_status_str": (ctypes.c_char_p, [_I]),
     "fa_last_hip_error": (_I, []),
     "fa_last_hip_error_str": (ctypes.c_char_p, []),
+    "fa_debug_flags": (_I, [_P, _I]),
     "fa_fwd": (_I, [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _F,
                     _P]),
     "fa_fwd_fp8": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P,
@@ -63,20 +70,25 @@ class FaError(RuntimeError):
 _lib = None
 
 
+def load(path):
+    """Open one build of the library and attach the declared signatures."""
+    if not os.path.exists(path):
+        raise LibraryMissing(
+            f"{path} is not built: run "
+            "`python -m exact_io_aware_15_amd.build` (needs ROCm hipcc)")
+    handle = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
 def lib():
-    """Load libfa355.so once and attach the declared signatures."""
+    """The library every wrapper calls (loaded once, from LIB_PATH)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise LibraryMissing(
-                f"{LIB_PATH} is not built: run "
-                "`python -m exact_io_aware_15_amd.build` (needs ROCm hipcc)")
-        handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = handle
+        _lib = load(LIB_PATH)
     return _lib
 
 

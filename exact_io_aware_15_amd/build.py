@@ -2,8 +2,11 @@
 
 Run as ``python -m exact_io_aware_15_amd.build``.  Each ``.hip`` source under
 ``csrc/`` is compiled to an object under ``_build/`` (in parallel), then the
-objects are linked into ``exact_io_aware_15_amd/libfa355.so``.  hipcc
-cross-compiles gfx950 code without a GPU present.
+objects are linked into ``exact_io_aware_15_amd/libfa355.so``.  The API source
+is compiled a second time with FA355_DEBUG defined and linked with the same
+kernel objects into ``libfa355_debug.so``, the build that checks the contents
+of the callers' device arrays.  hipcc cross-compiles gfx950 code without a GPU
+present.
 """
 
 import concurrent.futures as cf
@@ -19,6 +22,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa355.so")
+DEBUG_LIB = os.path.join(PKG, "libfa355_debug.so")
 
 ARCH = "gfx950"
 FLAGS = [
@@ -43,9 +47,15 @@ def hipcc():
 KERNEL_FLAGS = ["-fno-honor-nans"]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    extra = [] if os.path.basename(src) == "fa_api.hip" else KERNEL_FLAGS
+API = os.path.join(CSRC, "fa_api.hip")
+
+
+def _compile(src, verbose, debug=False):
+    obj = os.path.join(BUILD, os.path.basename(src) +
+                       (".debug.o" if debug else ".o"))
+    extra = [] if src == API else KERNEL_FLAGS
+    if debug:
+        extra = extra + ["-DFA355_DEBUG"]
     cmd = [hipcc()] + FLAGS + extra + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -55,14 +65,8 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False):
-    """Compile every source and link libfa355.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    workers = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
            "-o", tmp]
     if verbose:
@@ -70,7 +74,22 @@ def build(verbose=False):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    """Compile every source, link libfa355.so and libfa355_debug.so; returns
+    the path of the ordinary library."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    jobs = [(s, False) for s in srcs] + [(API, True)]
+    workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    api_obj, debug_obj = objs[srcs.index(API)], objs[-1]
+    kernels = [o for o in objs[:len(srcs)] if o != api_obj]
+    _link(kernels + [api_obj], LIB, verbose)
+    _link(kernels + [debug_obj], DEBUG_LIB, verbose)
     return LIB
 
 

@@ -57,6 +57,14 @@ bool drop_setup(float p, uint64_t seed, uint32_t offset, Dropout &dr) {
   return true;
 }
 
+// The debug build (FA355_DEBUG defined) puts the contract checks of
+// fa_check.hip on the stream ahead of each call's kernels.
+#ifdef FA355_DEBUG
+constexpr bool kChecks = true;
+#else
+constexpr bool kChecks = false;
+#endif
+
 int fwd_dense(int dtype, int B, int H, int N, int d, const void *q,
               const void *k, const void *v, void *o, float *m, float *l,
               const int32_t *kv_len, int causal, float scale,
@@ -69,6 +77,8 @@ int fwd_dense(int dtype, int B, int H, int N, int d, const void *q,
   a.scale = scale;
   a.c = (float)((double)scale * 1.4426950408889634);
   hipStream_t s = (hipStream_t)stream;
+  if (kChecks && kv_len)
+    if (hipError_t e = check_kv_len(kv_len, B, N, s)) return from_hip(e);
   if (dtype == FA_BF16) return from_hip(launch_fwd_bf16(a, d, causal != 0, s));
   return from_hip(launch_fwd_f32(a, d, causal != 0, s));
 }
@@ -92,7 +102,10 @@ int bwd_dense(int B, int H, int N, int d, const void *q, const void *k,
   a.B = B; a.H = H; a.N = N; a.BH = B * H;
   a.scale = scale;
   a.c = (float)((double)scale * 1.4426950408889634);
-  return from_hip(launch_bwd(a, d, causal != 0, (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  if (kChecks && kv_len)
+    if (hipError_t e = check_kv_len(kv_len, B, N, s)) return from_hip(e);
+  return from_hip(launch_bwd(a, d, causal != 0, s));
 }
 
 }  // namespace
@@ -164,7 +177,10 @@ int fa_fwd_fp8(int B, int H, int N, int d, const void *q, const void *k,
   a.o = (uint16_t *)o; a.m = m; a.l = l; a.kv_len = kv_len;
   a.B = B; a.H = H; a.N = N; a.BH = B * H;
   a.scale = scale;
-  return from_hip(launch_fwd_fp8(a, d, causal != 0, (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  if (kChecks && kv_len)
+    if (hipError_t e = check_kv_len(kv_len, B, N, s)) return from_hip(e);
+  return from_hip(launch_fwd_fp8(a, d, causal != 0, s));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -275,6 +291,9 @@ int fa_fwd_varlen(int dtype, int B, int H, int total, int max_seqlen, int d,
   a.scale = scale;
   a.c = (float)((double)scale * 1.4426950408889634);
   hipStream_t s = (hipStream_t)stream;
+  if (kChecks)
+    if (hipError_t e = check_cu_seqlens(cu_seqlens, B, total, max_seqlen, s))
+      return from_hip(e);
   if (dtype == FA_BF16) return from_hip(launch_fwd_bf16(a, d, causal != 0, s));
   return from_hip(launch_fwd_f32(a, d, causal != 0, s));
 }
@@ -315,7 +334,11 @@ int fa_bwd_varlen(int B, int H, int total, int max_seqlen, int d,
   a.B = B; a.H = H; a.N = max_seqlen; a.BH = B * H;
   a.scale = scale;
   a.c = (float)((double)scale * 1.4426950408889634);
-  return from_hip(launch_bwd(a, d, causal != 0, (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  if (kChecks)
+    if (hipError_t e = check_cu_seqlens(cu_seqlens, B, total, max_seqlen, s))
+      return from_hip(e);
+  return from_hip(launch_bwd(a, d, causal != 0, s));
 }
 
 int fa_prefill_paged(int B, int Hq, int Hkv, int d, int total_q, int max_q,
@@ -350,8 +373,16 @@ int fa_prefill_paged(int B, int Hq, int Hkv, int d, int total_q, int max_q,
   a.B = B; a.H = Hq; a.N = max_q; a.BH = B * Hq;
   a.scale = scale;
   a.c = (float)((double)scale * 1.4426950408889634);
-  return from_hip(launch_prefill_paged(a, d, causal != 0,
-                                       (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  if (kChecks) {
+    if (hipError_t e = check_cu_seqlens(cu_seqlens_q, B, total_q, max_q, s))
+      return from_hip(e);
+    if (hipError_t e = check_paged(seq_lens, cu_seqlens_q, block_table, B,
+                                   max_blocks_per_seq, block_size, num_blocks,
+                                   s))
+      return from_hip(e);
+  }
+  return from_hip(launch_prefill_paged(a, d, causal != 0, s));
 }
 
 size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
@@ -380,6 +411,7 @@ int fa_decode_paged(int B, int Hq, int Hkv, int d, const void *q,
   if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
   if (block_size != 16) return FA_E_UNSUPPORTED;
   if ((long long)B * max_blocks_per_seq > (1LL << 31) - 1 ||
+      (long long)max_blocks_per_seq * 16 > (1LL << 31) - 1 ||
       (long long)num_blocks * block_size * Hkv * d > (1LL << 40))
     return FA_E_SHAPE;
   const size_t need = fa_decode_workspace_bytes(B, Hq, d, num_splits);
@@ -402,7 +434,19 @@ int fa_decode_paged(int B, int Hq, int Hkv, int d, const void *q,
   a.num_splits = num_splits;
   a.scale = scale;
   a.c = (float)((double)scale * 1.4426950408889634);
-  return from_hip(launch_decode(a, d, (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  if (kChecks)
+    if (hipError_t e = check_paged(seq_lens, nullptr, block_table, B,
+                                   max_blocks_per_seq, block_size, num_blocks,
+                                   s))
+      return from_hip(e);
+  return from_hip(launch_decode(a, d, s));
+}
+
+int fa_debug_flags(uint32_t *flags, int clear) {
+  if (!kChecks) return FA_E_UNSUPPORTED;
+  if (!flags) return FA_E_NULLPTR;
+  return from_hip(read_contract_word(flags, clear != 0));
 }
 
 }  // extern "C"

@@ -99,4 +99,17 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t s);
 
+// Contract checks of the debug build (fa_check.hip).  Each launches one small
+// kernel on `s` that reads the named device arrays (and nothing else) and ORs
+// FA_CHECK_* bits into the current device's contract word.  cu_q may be NULL
+// (decode: no new-token counts to compare seq_lens against).
+hipError_t check_kv_len(const int32_t *kv_len, int B, int N, hipStream_t s);
+hipError_t check_cu_seqlens(const int32_t *cu, int B, int total, int max_len,
+                            hipStream_t s);
+hipError_t check_paged(const int32_t *seq_lens, const int32_t *cu_q,
+                       const int32_t *block_table, int B, int max_blocks,
+                       int block_size, int num_blocks, hipStream_t s);
+// Waits for the device, returns its contract word, and zeroes it if asked.
+hipError_t read_contract_word(uint32_t *word, bool clear);
+
 }  // namespace fa355

@@ -18,7 +18,9 @@
  *     returns a negative fa_status and has no side effect.  A launch failure
  *     reported by the HIP runtime returns FA_E_HIP.  The contents of device
  *     arrays (kv_len values, block-table entries, sequence lengths) are the
- *     caller's contract and are not checked.
+ *     caller's contract: the kernels clamp malformed values so that no access
+ *     leaves the buffers, but the results are then unspecified.  The debug
+ *     build of the library checks these contents (fa_debug_flags).
  *   - Tensors are contiguous, row-major, with the layouts stated per argument.
  *     bf16 means IEEE bfloat16 storage; results are rounded to nearest even.
  *   - The score scale is applied before the row max: S = scale * Q K^T.  S12's
@@ -56,6 +58,40 @@ const char *fa_status_str(int status);
  */
 int fa_last_hip_error(void);
 const char *fa_last_hip_error_str(void);
+
+/*
+ * Debug build.  The library built with FA355_DEBUG defined (libfa355_debug.so
+ * beside libfa355.so) runs, on the call's stream and ahead of the call's own
+ * kernels, a small check of every device array whose contents the call
+ * relies on, and ORs a bit per kind of violation into a word kept on each
+ * device.  The call's kernels then run exactly as in the ordinary build, so
+ * outputs are unchanged; the check adds one launch per contract array.
+ *
+ *   FA_CHECK_KV_LEN       a kv_len[b] outside [0, N].
+ *   FA_CHECK_CU_SEQLENS   cu_seqlens not 0 = cu[0] <= cu[1] <= ... <= cu[B]
+ *                         = total, or a sequence longer than max_seqlen
+ *                         (max_q for fa_prefill_paged).
+ *   FA_CHECK_SEQ_LENS     a seq_lens[b] outside [0, max_blocks_per_seq *
+ *                         block_size], or (fa_prefill_paged) smaller than the
+ *                         sequence's new-token count.
+ *   FA_CHECK_BLOCK_TABLE  a block-table entry the call reads (t <
+ *                         ceil(seq_len / block_size), seq_len clamped as the
+ *                         kernels clamp it) outside [0, num_blocks).
+ *
+ * fa_debug_flags waits for all work on the current device, stores that
+ * device's word in *flags and, if clear is nonzero, resets the word to 0.
+ * The word is sticky: it keeps the bits of every call since the last clear.
+ * Returns FA_E_NULLPTR for a NULL flags, FA_E_HIP if the runtime fails, and
+ * FA_E_UNSUPPORTED (touching nothing) in the ordinary build, which checks
+ * nothing.
+ */
+enum {
+  FA_CHECK_KV_LEN = 1,
+  FA_CHECK_CU_SEQLENS = 2,
+  FA_CHECK_SEQ_LENS = 4,
+  FA_CHECK_BLOCK_TABLE = 8
+};
+int fa_debug_flags(uint32_t *flags, int clear);
 
 /*
  * fa_fwd -- exact attention forward, O = softmax(scale * Q K^T) V.
@@ -314,6 +350,8 @@ int fa_bwd_varlen(int B, int H, int total, int max_seqlen, int d,
  *   v_cache        [num_blocks, Hkv, block_size, d] bf16, holding the K/V of
  *                  every token of each sequence, its new tokens included.
  *   block_size     16.
+ *   max_blocks_per_seq  >= 1, with B * max_blocks_per_seq and
+ *                  max_blocks_per_seq * 16 below 2^31 (else FA_E_SHAPE).
  *   block_table    device int32 [B, max_blocks_per_seq]; entries for t <
  *                  ceil(seq_len/16) must be in [0, num_blocks) (others are
  *                  clamped into that range, giving unspecified results).
@@ -360,6 +398,9 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
  *                Slots past a sequence's length are never read into the
  *                arithmetic (they may hold anything, NaN included).
  *   block_size   tokens per block; 16.
+ *   max_blocks_per_seq  >= 1; B * max_blocks_per_seq and
+ *                max_blocks_per_seq * block_size must stay below 2^31
+ *                (else FA_E_SHAPE).
  *   block_table  device int32 [B, max_blocks_per_seq]; entries for t <
  *                ceil(seq_len/block_size) must be in [0, num_blocks).  An
  *                entry outside that range is skipped (its tokens are treated

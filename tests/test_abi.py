@@ -38,6 +38,31 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_both_builds_export_every_symbol():
+    for path in (_lib.RELEASE_LIB_PATH, _lib.DEBUG_LIB_PATH):
+        if not os.path.exists(path):
+            pytest.skip(f"{path} not built")
+        handle = _lib.load(path)
+        for n in declared_functions():
+            assert hasattr(handle, n), (path, n)
+
+
+def test_debug_flags_without_device():
+    """The ordinary build checks nothing and says so; the debug build rejects
+    a NULL destination before touching the device."""
+    for path in (_lib.RELEASE_LIB_PATH, _lib.DEBUG_LIB_PATH):
+        if not os.path.exists(path):
+            pytest.skip(f"{path} not built")
+    release = _lib.load(_lib.RELEASE_LIB_PATH)
+    word = ctypes.c_uint32(7)
+    assert release.fa_debug_flags(ctypes.byref(word), 1) == -3
+    assert release.fa_debug_flags(NULL, 0) == -3
+    assert word.value == 7
+    debug = _lib.load(_lib.DEBUG_LIB_PATH)
+    assert debug.fa_debug_flags(NULL, 0) == -1
+    assert debug.fa_debug_flags(NULL, 1) == -1
+
+
 def test_status_strings(lib):
     for code in range(-5, 1):
         s = lib.fa_status_str(code).decode()
@@ -108,6 +133,10 @@ def test_decode_workspace_and_validation(lib):
     assert call(d=96) == -3
     assert call(bs=32) == -3
     assert call(ws_bytes=ws - 4) == -4
+    # a capacity of max_blocks_per_seq * 16 tokens must fit an int
+    assert lib.fa_decode_paged(1, 32, 8, 128, FAKE, FAKE, FAKE, 100, 16, FAKE,
+                               1 << 27, FAKE, 8, 0.1, FAKE, FAKE, ws,
+                               NULL) == -2
 
 
 def test_last_hip_error_starts_clear(lib):
