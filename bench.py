@@ -20,8 +20,19 @@ bf16).  The printed JSON line reports:
                when the kernels changed after the counters were taken.
   cpu_baseline the fp64 oracle on a bounded sample of the same workload, on
                this host's cores (a reported baseline, not a target).
+  fwd, bwd     mean, p10, p50 and p90 of each call's duration (hot cache:
+               back-to-back steps).
+  cold_cache   the same calls each timed after a 512 MiB buffer has been
+               read, so neither L2 nor the 256 MB MALL holds their inputs (a
+               read, not a write: written lines would be dirty, and their
+               write-back would land inside the timed call).
+  limiter      matrix-core busy, VALU busy and co-issue fractions of the
+               step's kernels from rocprofv3 SQ counters (committed summary,
+               null when the kernels changed after it was taken).
   sweep        the other workloads: forward / backward TFLOP/s and the paged
-               decode's bandwidth against 8 TB/s.
+               decode's bandwidth against 8 TB/s (calls rotate over three
+               copies of the 311 MB cache so that none finds its K/V in
+               MALL; the rate on one copy is reported beside it).
 """
 
 import argparse
@@ -38,6 +49,9 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+BUSY_FILE = os.path.join(ROOT, "profiles", "busy_counters.json")
+FLUSH_BYTES = 512 << 20     # > L2 (8 x 4 MB) + MALL (256 MB)
+DECODE_COPIES = 3           # 3 x 311 MB of paged cache > 2 x MALL
 
 
 # ---------------------------------------------------------------- IO model --
@@ -99,6 +113,11 @@ def parse():
                     help="time only this sweep workload (or "
                          "paged_chunked_prefill) and print its entry")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="skip the comparison timings (cold-cache step, "
+                         "single-copy decode): for profiling runs, so that "
+                         "every traced dispatch is one the reported rates "
+                         "count")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many "
@@ -180,9 +199,18 @@ class Attn:
                            workspace=self.ws)
 
 
-def time_step(attn, steps, warmup, backward=True):
+def percentiles(ms):
+    """p10 / p50 / p90 of a list of durations (nearest rank)."""
+    xs = sorted(ms)
+    pick = lambda q: xs[min(len(xs) - 1, int(q * len(xs)))]  # noqa: E731
+    return {"p10": round(pick(0.1), 4), "p50": round(pick(0.5), 4),
+            "p90": round(pick(0.9), 4)}
+
+
+def time_step(attn, steps, warmup, backward=True, per_call=None):
     """Run warmup steps, then `steps` timed steps with events around each
-    forward and backward call; returns mean ms of step, fwd and bwd."""
+    forward and backward call; returns mean ms of step, fwd and bwd (and,
+    if per_call is a dict, fills it with each call's percentiles)."""
     torch = attn.torch
     for _ in range(warmup):
         o, m, l = attn.fwd()
@@ -205,10 +233,40 @@ def time_step(attn, steps, warmup, backward=True):
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps if backward \
         else 0.0
     step_ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
+    if per_call is not None:
+        per_call["fwd"] = percentiles([e[0].elapsed_time(e[1]) for e in ev])
+        if backward:
+            per_call["bwd"] = percentiles([e[1].elapsed_time(e[2])
+                                           for e in ev])
     return step_ms, fwd_ms, bwd_ms, wall
 
 
-def decode_bench(steps, warmup, splits=None):
+def time_cold(torch, calls, reps):
+    """Each of `calls` (functions run in order, each given the previous
+    one's result) timed `reps` times right after FLUSH_BYTES have been
+    read on the same stream; returns the median ms of each."""
+    scratch = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+           for _ in calls] for _ in range(reps)]
+    for i in range(reps):
+        prev = None
+        for j, fn in enumerate(calls):
+            scratch.sum()
+            ev[i][j][0].record()
+            prev = fn(prev)
+            ev[i][j][1].record()
+    torch.cuda.synchronize()
+    del scratch
+    return [percentiles([ev[i][j][0].elapsed_time(ev[i][j][1])
+                         for i in range(reps)])["p50"]
+            for j in range(len(calls))]
+
+
+def decode_bench(steps, warmup, splits=None, compare=True):
+    """Back-to-back decode calls, rotating over DECODE_COPIES copies of the
+    paged cache (a serving step reads each layer's cache once, so no call
+    should find its K/V in cache); the same on a single copy is reported
+    beside it."""
     import numpy as np
     import torch
     import exact_io_aware_15_amd as fa
@@ -217,22 +275,31 @@ def decode_bench(steps, warmup, splits=None):
     w = WORKLOADS["paged_gqa_decode"]
     q, cache = w.decode_inputs(poison_tails=False)
     qd = to_device(q)
-    kc, vc = to_device(cache.k_cache), to_device(cache.v_cache)
+    kcs = [to_device(cache.k_cache) for _ in range(DECODE_COPIES)]
+    vcs = [to_device(cache.v_cache) for _ in range(DECODE_COPIES)]
     table = torch.from_numpy(cache.block_table).cuda()
     lens = torch.from_numpy(cache.seq_lens).cuda()
     splits = w.splits if splits is None else splits
     ws = torch.empty(fa.decode_workspace_bytes(w.B, w.H, w.d, splits),
                      dtype=torch.uint8, device="cuda")
-    for _ in range(warmup):
-        fa.decode_paged(qd, kc, vc, table, lens, splits, workspace=ws)
-    torch.cuda.synchronize()
-    e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
-    e0.record()
-    for _ in range(steps):
-        fa.decode_paged(qd, kc, vc, table, lens, splits, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+
+    def run(copies):
+        for i in range(warmup):
+            c = i % copies
+            fa.decode_paged(qd, kcs[c], vcs[c], table, lens, splits,
+                            workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        e0.record()
+        for i in range(steps):
+            c = i % copies
+            fa.decode_paged(qd, kcs[c], vcs[c], table, lens, splits,
+                            workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    ms = run(DECODE_COPIES)
+    same_ms = run(1) if compare else None
     total_len = int(np.sum(cache.seq_lens))
     # K and V rows read: len * Hkv * d * 2 bytes each
     kv_bytes = total_len * w.Hkv * w.d * 2 * 2
@@ -241,12 +308,19 @@ def decode_bench(steps, warmup, splits=None):
             "kv_bytes": kv_bytes,
             "GB/s": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "cache_copies": DECODE_COPIES,
+            "same_copy": None if same_ms is None else {
+                "ms": round(same_ms, 4),
+                "GB/s": round(kv_bytes / same_ms / 1e6, 1),
+                "note": "back-to-back on one copy: part of the K/V is "
+                        "still in MALL"},
             "roofline": {"kernel": "fa_decode_paged (decode_split_kernel + "
                                    "decode_merge_kernel launches)",
                          "bound": "hbm", "achieved": round(gbs, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": traffic_for("fa_decode_paged")}}
+                         "traffic": traffic_for("fa_decode_paged")},
+            "limiter": busy_counters(w.name)}
 
 
 def prefill_bench(steps, warmup):
@@ -324,6 +398,7 @@ def sweep_one(name, steps, warmup, out):
         r["speedup_fwd"] = round(dfwd / fwd_ms, 2)
         r["speedup_bwd"] = round(dbwd / bwd_ms, 2)
         del dense
+    r["limiter"] = busy_counters(name)
     out[name] = r
     del attn
     return r
@@ -374,6 +449,21 @@ def cpu_baseline(w, budget_s):
                       f"of {w.name} ({el:.1f} s)"}
 
 
+def busy_counters(workload):
+    """Per-kernel fractions of the cycles in which the matrix cores were
+    busy, the VALU was issuing, and both at once, from the committed SQ
+    counter summary of `workload`, if it was taken on the current kernel
+    sources (else None)."""
+    try:
+        with open(BUSY_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("workloads", {}).get(workload)
+
+
 def traffic_for(call):
     """HBM bytes per call from the committed counter summary, if it was
     taken on the current kernel sources."""
@@ -409,7 +499,9 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_bytes, "steps": args.steps}))
         return
     if args.decode_only:
-        print(json.dumps(decode_bench(args.steps, args.warmup)), flush=True)
+        print(json.dumps(decode_bench(args.steps, args.warmup,
+                                      compare=not args.no_compare)),
+              flush=True)
         return
     if args.sweep_only:
         if args.sweep_only == "paged_chunked_prefill":
@@ -420,8 +512,19 @@ def main():
         return
     w = WORKLOADS[args.workload]
     attn = Attn(w)
+    per_call = {}
     step_ms, fwd_ms, bwd_ms, wall_ms = time_step(attn, args.steps,
-                                                 args.warmup)
+                                                 args.warmup,
+                                                 per_call=per_call)
+    cold = None
+    if not args.no_compare:
+        cf, cb = time_cold(
+            torch, [lambda _: attn.fwd(), lambda oml: attn.bwd(*oml)],
+            max(10, args.steps // 2))
+        cold = {"fwd_ms_p50": round(cf, 4), "bwd_ms_p50": round(cb, 4),
+                "fwd_tflops": round(w.fwd_flops() / cf / 1e9, 1),
+                "bwd_tflops": round(w.bwd_flops() / cb / 1e9, 1),
+                "note": f"{FLUSH_BYTES >> 20} MiB written before each call"}
     flops = w.fwd_flops() + w.bwd_flops()
     value = flops / step_ms / 1e9
     if bwd_ms >= fwd_ms:
@@ -448,10 +551,12 @@ def main():
                    "d": w.d, "causal": w.causal, "dtype": w.dtype,
                    "fwd_flops": w.fwd_flops(), "bwd_flops": w.bwd_flops()},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "fwd": {"ms": round(fwd_ms, 4),
+        "fwd": {"ms": round(fwd_ms, 4), **per_call["fwd"],
                 "tflops": round(w.fwd_flops() / fwd_ms / 1e9, 1)},
-        "bwd": {"ms": round(bwd_ms, 4),
+        "bwd": {"ms": round(bwd_ms, 4), **per_call["bwd"],
                 "tflops": round(w.bwd_flops() / bwd_ms / 1e9, 1)},
+        "cold_cache": cold,
+        "limiter": busy_counters(w.name),
         "host_wall_ms_per_step": round(wall_ms, 4),
         "roofline": {"kernel": kern, "bound": "mfma",
                      "achieved": round(achieved, 1),

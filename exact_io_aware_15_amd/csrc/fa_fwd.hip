@@ -29,9 +29,11 @@ namespace {
 // reference, and l is converted to the true max at the end.
 constexpr float kRescaleLog2 = 8.0f;
 
+// MINW: waves per SIMD the register allocation must allow (4 caps a lane at
+// 128 VGPRs; 2 lets the compiler take what it needs).
 template <int D, int QPW, bool CAUSAL, bool PADDED, bool PAGED = false,
-          bool SPARSE = false, bool DROP = false>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+          bool SPARSE = false, bool DROP = false, int MINW = 2>
+__global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int QB = QPW / 32;                    // 32-query blocks per wave
   constexpr int BR = 4 * QPW;                     // queries per workgroup
   constexpr int BC = 64;                          // keys per tile
@@ -417,15 +419,32 @@ __global__ __launch_bounds__(64, 1) void fwd_f32_kernel(FwdArgs a) {
   }
 }
 
+// Key ranges up to this length run the d = 64 forward at 4 waves per SIMD:
+// the extra resident workgroups hide more latency on short rows (measured
+// +7-9% at N = 1K and on the ragged prefill, neutral at 4K), while on long
+// rows the extra concurrent K/V streams per XCD cost L2 hits (-3% at 64K).
+constexpr int kFourWaveMaxN = 8192;
+
 template <int D, bool CAUSAL>
 hipError_t fwd_bf16_dispatch_pad(const FwdArgs &a, hipStream_t s) {
-  // 64 queries per wave at d = 64 (two query blocks share every K / V
-  // fragment read from LDS); 32 at d = 128, where the accumulator is twice
-  // as large.
+  // 32 queries per wave (one 32-query block), 4 waves per workgroup.
   constexpr int QPW = 32;
   const int nqt = (a.N + 4 * QPW - 1) / (4 * QPW);
   dim3 grid((unsigned)(nqt * a.BH)), block(256);
   const bool drop = a.drop.thr != 0;
+  if constexpr (D == 64) {
+    if (!drop && a.N <= kFourWaveMaxN) {
+      if (a.kv_len)
+        hipLaunchKernelGGL(
+            (fwd_bf16_kernel<D, QPW, CAUSAL, true, false, false, false, 4>),
+            grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL(
+            (fwd_bf16_kernel<D, QPW, CAUSAL, false, false, false, false, 4>),
+            grid, block, 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if (a.kv_len) {
     if (drop)
       hipLaunchKernelGGL(

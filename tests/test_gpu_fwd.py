@@ -149,3 +149,22 @@ def test_fwd_workload_sampled_rows(name):
         rng.integers(0, w.N, size=22)]))
     print(f"fwd workload {name} (rows {rows.size})", flush=True)
     _check(name, q, k, v, w.causal, None, BF16_TOL, rows=rows)
+
+
+# d = 64 rows up to 8192 keys run at four waves per SIMD, longer ones at
+# three: both sides of the switch, padded and not, on sampled rows.
+@pytest.mark.parametrize("N,causal,kv_len", [
+    (8192, True, [8192, 5000]),
+    (8193, True, None),
+    (8257, False, [8257, 7000]),
+    (8257, True, [3000, 8200]),
+])
+def test_fwd_d64_either_side_of_the_occupancy_switch(N, causal, kv_len):
+    B, H, d = 2, 1, 64
+    q, k, v = (normal((B, H, N, d), 9600 + N, t, "bf16") for t in range(3))
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 2999, 3000, 4999, 5000,
+                                      N - 65, N - 64, N - 1],
+                                     np.random.default_rng(N).integers(
+                                         0, N, size=12)]))
+    print(f"fwd d=64 N={N} causal={causal} kv_len={kv_len}", flush=True)
+    _check(f"occ N={N}", q, k, v, causal, kv_len, BF16_TOL, rows=rows)
