@@ -524,7 +524,7 @@ def main():
         cold = {"fwd_ms_p50": round(cf, 4), "bwd_ms_p50": round(cb, 4),
                 "fwd_tflops": round(w.fwd_flops() / cf / 1e9, 1),
                 "bwd_tflops": round(w.bwd_flops() / cb / 1e9, 1),
-                "note": f"{FLUSH_BYTES >> 20} MiB written before each call"}
+                "note": f"{FLUSH_BYTES >> 20} MiB read before each call"}
     flops = w.fwd_flops() + w.bwd_flops()
     value = flops / step_ms / 1e9
     if bwd_ms >= fwd_ms:
