@@ -161,10 +161,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   // Q / dO step fills: uniform-base DMA for whole steps, the clamped
   // (out-of-line) fill for the ragged last one.
   const DmaOffsets<D, BR> doff;
+  const uint32_t slice_bytes = (uint32_t)N * D * 2;  // N <= 2^20, d <= 128
   auto load_step = [&](int q1, int b2) {
     if (q1 + BR <= N) {
-      dma_tile_at<D, BR>(Qs[b2], qg + (size_t)q1 * D, doff);
-      dma_tile_at<D, BR>(dOs[b2], dog + (size_t)q1 * D, doff);
+      dma_tile_at<D, BR>(Qs[b2], qg, slice_bytes, (uint32_t)q1 * D * 2, doff);
+      dma_tile_at<D, BR>(dOs[b2], dog, slice_bytes, (uint32_t)q1 * D * 2, doff);
     } else {
       dma_tile_tail<D, BR>(Qs[b2], qg, q1, N - 1);
       dma_tile_tail<D, BR>(dOs[b2], dog, q1, N - 1);
@@ -386,10 +387,11 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
   // K / V tile fills: uniform-base DMA for whole tiles, the clamped
   // (out-of-line) fill for the tail.
   const DmaOffsets<D, BC> doff;
+  const uint32_t slice_bytes = (uint32_t)N * D * 2;  // N <= 2^20, d <= 128
   auto load_tile = [&](int k0, int b2) {
     if (k0 + BC <= kv_valid) {
-      dma_tile_at<D, BC>(Ks[b2], kg + (size_t)k0 * D, doff);
-      dma_tile_at<D, BC>(Vs[b2], vg + (size_t)k0 * D, doff);
+      dma_tile_at<D, BC>(Ks[b2], kg, slice_bytes, (uint32_t)k0 * D * 2, doff);
+      dma_tile_at<D, BC>(Vs[b2], vg, slice_bytes, (uint32_t)k0 * D * 2, doff);
     } else {
       dma_tile_tail<D, BC>(Ks[b2], kg, k0, kv_valid - 1);
       dma_tile_tail<D, BC>(Vs[b2], vg, k0, kv_valid - 1);

@@ -298,7 +298,7 @@ __device__ __forceinline__ void lds_store_chunk(uint16_t *tile, int row,
 
 // Fills an LDS operand tile of ROWS x W bf16 (swizzled, rows in row_perm
 // order) from rows row0 .. row0+ROWS-1 of a row-major [*, W] bf16 matrix by
-// direct DMA (global_load_lds_dwordx4).  One wave instruction fills 1 KB of
+// direct DMA (global_load_lds_dwordx4), issued by four waves.  One wave instruction fills 1 KB of
 // LDS with lane i writing bytes 16i..16i+15, so each lane fetches the global
 // chunk that belongs at its slot.  Rows past last_row read row last_row
 // instead (finite data the caller masks); last_row must be >= 0.  The loads
@@ -345,22 +345,32 @@ struct DmaOffsets {
   }
 };
 
-// dma_tile for rows row0 .. row0+ROWS-1 all valid: src_rows points at row
-// row0 (a wave-uniform address), o holds the per-lane offsets.
+// dma_tile for rows row0 .. row0+ROWS-1 all valid, through a raw buffer
+// resource over the `bytes` bytes of the matrix slice at `base` (word 3 =
+// 32-bit data format, no stride): each load names a byte offset as a per-lane
+// register (o) plus a scalar (row0_bytes = row0 * W * 2), so filling a tile
+// costs no vector address arithmetic, and an offset past `bytes` would read
+// zeros instead of leaving the slice.  The LDS destination of each wave
+// instruction is wave-uniform and set up by scalar instructions.
 template <int W, int ROWS>
-__device__ __forceinline__ void dma_tile_at(uint16_t *tile,
-                                            const uint16_t *src_rows,
+__device__ __forceinline__ void dma_tile_at(uint16_t *tile, const void *base,
+                                            uint32_t bytes,
+                                            uint32_t row0_bytes,
                                             const DmaOffsets<W, ROWS> &o) {
-  const int wave = threadIdx.x >> 6;
+  // The resource type exists only for the GPU target; the host pass of the
+  // compilation (which never runs device code) sees an empty body.
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto src = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int u = 0; u < DmaOffsets<W, ROWS>::SEGS / 4; ++u) {
     const int seg = wave + 4 * u;
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void *)(
-            (const char *)src_rows + o.off[u]),
-        (__attribute__((address_space(3))) void *)(tile + seg * 512), 16, 0,
-        0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src, (__attribute__((address_space(3))) void *)(tile + seg * 512), 16,
+        o.off[u], row0_bytes, 0, 0);
   }
+#endif
 }
 
 // dma_tile kept out of line, for the rare tail tile of a loop whose other

@@ -29,6 +29,174 @@ namespace {
 // reference, and l is converted to the true max at the end.
 constexpr float kRescaleLog2 = 8.0f;
 
+// One key tile of the forward for the calling wave's QB 32-query blocks
+// (queries qw .. qw + 32*QB - 1) against the 64 keys k0 .. k0+63 staged in
+// Kt / Vt: S^T = K Q^T, the mask (diagonal and tail tiles only), the
+// running-max update, p = exp2(c*s - c*m_ref) rounded to bf16 once, l += sum p
+// and O^T += V^T P^T.  A tile wholly above the causal diagonal is skipped.
+template <int D, int QB, bool CAUSAL, bool DROP>
+__device__ __forceinline__ void fwd_tile(
+    const uint16_t *Kt, const uint16_t *Vt, int k0, int qw, int kv_valid,
+    int qoff, int bh, float c, const Dropout &drop,
+    const bf16x8 (&qf)[QB][D / 16], f32x16 (&oacc)[QB][D / 32],
+    float (&m_ref)[QB], float (&m_max)[QB], float (&l_run)[QB]) {
+  constexpr int QPW = 32 * QB;
+  constexpr int BC = 64;
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 31, hh = lane >> 5;
+  if (CAUSAL && k0 > qw + QPW - 1 + qoff) return;  // above the diagonal
+  // S^T = K Q^T for every (key block, query block).
+  f32x16 s[QB][2];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+  // ks outer: the two key blocks' accumulations alternate, so each
+  // MFMA's predecessor in the pipe is independent of it.
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 kf = lds_row_frag<D>(Kt, kb * 32 + ln, ks * 16 + 8 * hh);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        s[qb][kb] = mfma32(kf, qf[qb][ks], s[qb][kb]);
+    }
+
+  // Online softmax per query block.  Register r of key block kb holds
+  // key k0 + 32*kb + 16*(r/8) + 8*hh + (r%8) of this lane's query.
+  // pv[qb][kb][s2] is the B operand (8 consecutive keys) of P V.
+  u32x4 pv[QB][2][2];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qbase = qw + 32 * qb;
+    const int qi = qbase + ln;
+    const bool need_mask =
+        (k0 + BC > kv_valid) || (CAUSAL && k0 + BC - 1 > qbase + qoff);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
+          const bool masked =
+              key >= kv_valid || (CAUSAL && key > qi + qoff);
+          s[qb][kb][r] = masked ? -INFINITY : s[qb][kb][r];
+        }
+    }
+    // A chain max(max(mx, a), b) per pair: one v_max3_f32 per two scores.
+    float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2)
+        mx = fmaxf(fmaxf(mx, s[qb][kb][r]), s[qb][kb][r + 1]);
+    mx = max_xor32(mx);
+    m_max[qb] = fmaxf(m_max[qb], mx);
+    // Move the reference only when some row's max outgrew it by more than
+    // kRescaleLog2 in log2 units (a wave-uniform branch; the empty asm keeps
+    // it a branch).
+    if (__any((m_max[qb] - m_ref[qb]) * c > kRescaleLog2)) {
+      asm volatile("" ::: "memory");
+      const float alpha = fast_exp2((m_ref[qb] - m_max[qb]) * c);
+      m_ref[qb] = m_max[qb];
+      l_run[qb] *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[qb][cb][r] *= alpha;
+    }
+    const float mc = m_ref[qb] * c;
+    // Dropout: this lane's 16 random bytes per key block (its query,
+    // group 2*(key block) + hh); l keeps the undropped sum.
+    u32x4 rnd[2];
+    if (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        rnd[kb] = drop_bytes(drop, qi, 2 * ((k0 >> 5) + kb) + hh, bh);
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 8 * s2 + 2 * i;
+          const float p0 = fast_exp2(fmaf(s[qb][kb][r], c, -mc));
+          const float p1 = fast_exp2(fmaf(s[qb][kb][r + 1], c, -mc));
+          const uint32_t pu = pack_bf16x2(p0, p1);
+          lsum = dot2_ones(pu, lsum);
+          if (DROP) {
+            const uint32_t keep =
+                (drop_keep(rnd[kb], r, drop.thr) ? 0xffffu : 0u) |
+                (drop_keep(rnd[kb], r + 1, drop.thr) ? 0xffff0000u : 0u);
+            pv[qb][kb][s2][i] = pu & keep;
+          } else {
+            pv[qb][kb][s2][i] = pu;
+          }
+        }
+    l_run[qb] += lsum;
+  }
+
+  // O^T += V^T P^T: the V^T fragment is read once (transposing LDS load)
+  // and used for every query block.  A query block whose keys are all
+  // masked contributes p = 0.
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int cb = 0; cb < D / 32; ++cb) {
+        const bf16x8 vf = lds_tr_frag<D>(Vt, kb * 32 + 16 * s2, cb * 32);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          oacc[qb][cb] = mfma32(vf, __builtin_bit_cast(bf16x8, pv[qb][kb][s2]),
+                                oacc[qb][cb]);
+      }
+}
+
+// Epilogue for one lane's query qi: O = o / l (0 for a row with no visible
+// key) for the 32-column blocks cb_lo .. cb_hi-1 of the accumulator, and, if
+// stats, m in natural units and l referred to the true max.  l_ref is the
+// row's full sum (both lane halves) against the reference max m_ref.
+template <int D, bool DROP>
+__device__ __forceinline__ void fwd_store_rows(const FwdArgs &a, size_t hoff,
+                                               size_t row0, int qi, int N,
+                                               float l_ref, float m_ref,
+                                               float m_max,
+                                               const f32x16 (&oacc)[D / 32],
+                                               int cb_lo, int cb_hi,
+                                               bool stats) {
+  if (qi >= N) return;
+  const int hh = (threadIdx.x & 63) >> 5;
+  // Kept probabilities carry the factor 256 / (256 - thr).
+  const float num = DROP ? a.drop.keep_scale : 1.0f;
+  const float inv = l_ref > 0.f ? num / l_ref : 0.f;
+  uint16_t *og = (uint16_t *)a.o + hoff + (size_t)qi * D;
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) {
+    if (cb < cb_lo || cb >= cb_hi) continue;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c0 = cb * 32 + 8 * g + 4 * hh;
+      u32x2 w2;
+      w2[0] = pack_bf16x2(oacc[cb][4 * g] * inv, oacc[cb][4 * g + 1] * inv);
+      w2[1] =
+          pack_bf16x2(oacc[cb][4 * g + 2] * inv, oacc[cb][4 * g + 3] * inv);
+      *reinterpret_cast<u32x2 *>(og + c0) = w2;
+    }
+  }
+  if (stats && a.m != nullptr) {
+    const size_t ri = row0 + qi;
+    const float l_true = l_ref * fast_exp2((m_ref - m_max) * a.c);
+    a.m[ri] = l_ref > 0.f ? m_max * a.scale : -INFINITY;
+    a.l[ri] = l_ref > 0.f ? l_true : 0.f;
+  }
+}
+
 // MINW: waves per SIMD the register allocation must allow (4 caps a lane at
 // 128 VGPRs; 2 lets the compiler take what it needs).
 template <int D, int QPW, bool CAUSAL, bool PADDED, bool PAGED = false,
@@ -113,7 +281,6 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
     l_run[qb] = 0.f;       // over this lane's half of the keys
   }
   const float c = a.c;
-  const float thr = kRescaleLog2 / c;  // threshold in raw score units
 
   // Global -> LDS staging by direct DMA; keys past kv_valid read the last
   // valid key instead (finite data that the mask then excludes).  A paged
@@ -129,13 +296,18 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
   };
   int e_next[4] = {0, 0, 0, 0};
   const DmaOffsets<D, BC> doff;
+  // Whole tiles of a dense or packed slice go through buffer resources over
+  // the slice's N rows (N <= 2^20, d <= 128: under 2^28 bytes).
+  const uint32_t slice_bytes = PAGED ? 0u : (uint32_t)N * D * 2;
   auto load_tile = [&](int k0, int buf) {
     if (PAGED) {
       dma_tile_paged<D>(Ks[buf], kg, blk_stride, e_next, k0, kv_valid - 1);
       dma_tile_paged<D>(Vs[buf], vg, blk_stride, e_next, k0, kv_valid - 1);
     } else if (k0 + BC <= kv_valid) {  // whole tile valid: uniform base
-      dma_tile_at<D, BC>(Ks[buf], kg + (size_t)k0 * D, doff);
-      dma_tile_at<D, BC>(Vs[buf], vg + (size_t)k0 * D, doff);
+      dma_tile_at<D, BC>(Ks[buf], kg, slice_bytes, (uint32_t)k0 * D * 2,
+                         doff);
+      dma_tile_at<D, BC>(Vs[buf], vg, slice_bytes, (uint32_t)k0 * D * 2,
+                         doff);
     } else {
       dma_tile_tail<D, BC>(Ks[buf], kg, k0, kv_valid - 1);
       dma_tile_tail<D, BC>(Vs[buf], vg, k0, kv_valid - 1);
@@ -177,117 +349,8 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
     const uint16_t *Kt = Ks[buf];
     const uint16_t *Vt = Vs[buf];
 
-    if (!(CAUSAL && k0 > qw + QPW - 1 + qoff)) {  // else: above the diagonal
-      // S^T = K Q^T for every (key block, query block).
-      f32x16 s[QB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
-      // ks outer: the two key blocks' accumulations alternate, so each
-      // MFMA's predecessor in the pipe is independent of it.
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf = lds_row_frag<D>(Kt, kb * 32 + ln, ks * 16 + 8 * hh);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            s[qb][kb] = mfma32(kf, qf[qb][ks], s[qb][kb]);
-        }
-
-      // Online softmax per query block.  Register r of key block kb holds
-      // key k0 + 32*kb + 16*(r/8) + 8*hh + (r%8) of this lane's query.
-      // pv[qb][kb][s2] is the B operand (8 consecutive keys) of P V.
-      u32x4 pv[QB][2][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int qbase = qw + 32 * qb;
-        const int qi = qbase + ln;
-        const bool need_mask =
-            (k0 + BC > kv_valid) || (CAUSAL && k0 + BC - 1 > qbase + qoff);
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
-              const bool masked =
-                  key >= kv_valid || (CAUSAL && key > qi + qoff);
-              s[qb][kb][r] = masked ? -INFINITY : s[qb][kb][r];
-            }
-        }
-        float mx = fmaxf(s[qb][0][0], s[qb][0][1]);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2)
-            mx = fmaxf(mx, fmaxf(s[qb][kb][r], s[qb][kb][r + 1]));
-        mx = max_xor32(mx);
-        m_max[qb] = fmaxf(m_max[qb], mx);
-        // Move the reference only when some row's max outgrew it by > thr
-        // (a wave-uniform branch; the empty asm keeps it a branch).
-        if (__any(m_max[qb] - m_ref[qb] > thr)) {
-          asm volatile("" ::: "memory");
-          const float alpha = fast_exp2((m_ref[qb] - m_max[qb]) * c);
-          m_ref[qb] = m_max[qb];
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[qb][cb][r] *= alpha;
-        }
-        const float mc = m_ref[qb] * c;
-        // Dropout: this lane's 16 random bytes per key block (its query,
-        // group 2*(key block) + hh); l keeps the undropped sum.
-        u32x4 rnd[2];
-        if (DROP) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            rnd[kb] = drop_bytes(a.drop, qi, 2 * ((k0 >> 5) + kb) + hh, bh);
-        }
-        float lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 8 * s2 + 2 * i;
-              const float p0 = fast_exp2(fmaf(s[qb][kb][r], c, -mc));
-              const float p1 = fast_exp2(fmaf(s[qb][kb][r + 1], c, -mc));
-              const uint32_t pu = pack_bf16x2(p0, p1);
-              lsum = dot2_ones(pu, lsum);
-              if (DROP) {
-                const uint32_t keep =
-                    (drop_keep(rnd[kb], r, a.drop.thr) ? 0xffffu : 0u) |
-                    (drop_keep(rnd[kb], r + 1, a.drop.thr) ? 0xffff0000u : 0u);
-                pv[qb][kb][s2][i] = pu & keep;
-              } else {
-                pv[qb][kb][s2][i] = pu;
-              }
-            }
-        l_run[qb] += lsum;
-      }
-
-      // O^T += V^T P^T: the V^T fragment is read once (transposing LDS load)
-      // and used for every query block.  A query block whose keys are all
-      // masked contributes p = 0.
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int cb = 0; cb < D / 32; ++cb) {
-            const bf16x8 vf = lds_tr_frag<D>(Vt, kb * 32 + 16 * s2, cb * 32);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              oacc[qb][cb] = mfma32(vf, __builtin_bit_cast(bf16x8, pv[qb][kb][s2]),
-                                    oacc[qb][cb]);
-          }
-    }
+    fwd_tile<D, QB, CAUSAL, DROP>(Kt, Vt, k0, qw, kv_valid, qoff, bh, c,
+                                  a.drop, qf, oacc, m_ref, m_max, l_run);
 
     wait_dma();  // the next tile has landed
     __syncthreads();
@@ -302,35 +365,10 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
   // Epilogue: O = o / l (0 for a row with no visible key); m in natural
   // units and l referred to the true max.
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = qw + 32 * qb + ln;
-    const float l_ref = sum_xor32(l_run[qb]);
-    if (qi < N) {
-      // Kept probabilities carry the factor 256 / (256 - thr).
-      const float num = DROP ? a.drop.keep_scale : 1.0f;
-      const float inv = l_ref > 0.f ? num / l_ref : 0.f;
-      uint16_t *og = (uint16_t *)a.o + hoff + (size_t)qi * D;
-#pragma unroll
-      for (int cb = 0; cb < D / 32; ++cb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int c0 = cb * 32 + 8 * g + 4 * hh;
-          u32x2 w2;
-          w2[0] = pack_bf16x2(oacc[qb][cb][4 * g] * inv,
-                              oacc[qb][cb][4 * g + 1] * inv);
-          w2[1] = pack_bf16x2(oacc[qb][cb][4 * g + 2] * inv,
-                              oacc[qb][cb][4 * g + 3] * inv);
-          *reinterpret_cast<u32x2 *>(og + c0) = w2;
-        }
-      if (hh == 0 && a.m != nullptr) {
-        const size_t ri = sr.row0 + qi;
-        const float l_true =
-            l_ref * fast_exp2((m_ref[qb] - m_max[qb]) * c);
-        a.m[ri] = l_ref > 0.f ? m_max[qb] * a.scale : -INFINITY;
-        a.l[ri] = l_ref > 0.f ? l_true : 0.f;
-      }
-    }
-  }
+  for (int qb = 0; qb < QB; ++qb)
+    fwd_store_rows<D, DROP>(a, hoff, sr.row0, qw + 32 * qb + ln, N,
+                            sum_xor32(l_run[qb]), m_ref[qb], m_max[qb],
+                            oacc[qb], 0, D / 32, hh == 0);
 }
 
 // fp32 path: one thread per query, 16-key tiles staged in LDS, the same
