@@ -73,8 +73,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   constexpr int CPR = D / 8;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BR * D];
   __shared__ __attribute__((aligned(16))) uint16_t dOs[2][BR * D];
-  // Row statistics of the staged queries, interleaved (lse2, D) per query.
+  // Row statistics of the staged queries, interleaved (lse2, D) per query,
+  // and -D by query: the start value of the dP accumulator, so the matrix
+  // cores return dP - D (not with dropout, where D stays outside the mask).
   __shared__ __attribute__((aligned(16))) float LDs[2][2 * BR];
+  __shared__ __attribute__((aligned(16))) float NDs[2][BR];
 
   const int tid = threadIdx.x;
   // The wave index is uniform: readfirstlane lets the compiler see it, so
@@ -181,6 +184,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
       load_stats(q1, l_nx, d_nx);
       LDs[0][2 * tid] = l_nx;
       LDs[0][2 * tid + 1] = d_nx;
+      NDs[0][tid] = -d_nx;
     }
   }
   wait_dma();
@@ -200,6 +204,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t *Qt = Qs[buf];
     const uint16_t *dOt = dOs[buf];
     const float *LDt = LDs[buf];
+    const float *NDt = NDs[buf];
 
 #pragma unroll
     for (int qb = 0; qb < BR / 32; ++qb) {
@@ -208,6 +213,15 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+      if (!DROP) {  // dp starts at -D of register r's query
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 nd = *reinterpret_cast<const f32x4 *>(
+              &NDt[32 * qb + 16 * (j >> 1) + 8 * hh + 4 * (j & 1)]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[4 * j + e] = nd[e];
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const bf16x8 qf = lds_row_frag<D>(Qt, 32 * qb + ln, ks * 16 + 8 * hh);
@@ -252,7 +266,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                                 -st[2 * t + 1]);
             } else {
               pv[t] = p;
-              dsv[t] = p * (dp[r] - st[2 * t + 1]);
+              dsv[t] = p * dp[r];  // dp already holds dP - D
             }
           }
           pp[i] = pack_bf16x2(pv[0], pv[1]);
@@ -283,6 +297,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     if (has_next && tid < BR) {
       LDs[buf ^ 1][2 * tid] = l_nx;
       LDs[buf ^ 1][2 * tid + 1] = d_nx;
+      NDs[buf ^ 1][tid] = -d_nx;
     }
     wait_dma();
     __syncthreads();
