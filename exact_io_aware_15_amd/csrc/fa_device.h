@@ -363,12 +363,15 @@ __device__ __forceinline__ void dma_tile_at(uint16_t *tile, const void *base,
   const auto src = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // The tile offset is the same in every lane; stating so keeps it in a
+  // scalar register (a vector one would wrap each load in a waterfall loop).
+  const uint32_t soff = __builtin_amdgcn_readfirstlane(row0_bytes);
 #pragma unroll
   for (int u = 0; u < DmaOffsets<W, ROWS>::SEGS / 4; ++u) {
     const int seg = wave + 4 * u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         src, (__attribute__((address_space(3))) void *)(tile + seg * 512), 16,
-        o.off[u], row0_bytes, 0, 0);
+        o.off[u], soff, 0, 0);
   }
 #endif
 }
