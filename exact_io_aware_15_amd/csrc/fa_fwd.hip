@@ -69,6 +69,8 @@ __device__ __forceinline__ void fwd_tile(
   // key k0 + 32*kb + 16*(r/8) + 8*hh + (r%8) of this lane's query.
   // pv[qb][kb][s2] is the B operand (8 consecutive keys) of P V.
   u32x4 pv[QB][2][2];
+  float mcs[QB];
+  u32x4 rnd[QB][2];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qbase = qw + 32 * qb;
@@ -108,44 +110,47 @@ __device__ __forceinline__ void fwd_tile(
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[qb][cb][r] *= alpha;
     }
-    const float mc = m_ref[qb] * c;
+    mcs[qb] = m_ref[qb] * c;
     // Dropout: this lane's 16 random bytes per key block (its query,
     // group 2*(key block) + hh); l keeps the undropped sum.
-    u32x4 rnd[2];
     if (DROP) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        rnd[kb] = drop_bytes(drop, qi, 2 * ((k0 >> 5) + kb) + hh, bh);
+        rnd[qb][kb] = drop_bytes(drop, qi, 2 * ((k0 >> 5) + kb) + hh, bh);
     }
-    float lsum = 0.f;
+  }
+
+  // Per 32-key block: p = exp2(c*s - c*m_ref) rounded to bf16 (the same
+  // values feed l and the product), then O^T += V^T P^T for that block.  The
+  // block-0 products are issued before block 1's exponentials, so the
+  // matrix cores work on them while the VALU computes block 1.  The V^T
+  // fragment is read once (transposing LDS load) and used for every query
+  // block; a query block whose keys are all masked contributes p = 0.
+  float lsum[QB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+  for (int qb = 0; qb < QB; ++qb) lsum[qb] = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 8 * s2 + 2 * i;
-          const float p0 = fast_exp2(fmaf(s[qb][kb][r], c, -mc));
-          const float p1 = fast_exp2(fmaf(s[qb][kb][r + 1], c, -mc));
+          const float p0 = fast_exp2(fmaf(s[qb][kb][r], c, -mcs[qb]));
+          const float p1 = fast_exp2(fmaf(s[qb][kb][r + 1], c, -mcs[qb]));
           const uint32_t pu = pack_bf16x2(p0, p1);
-          lsum = dot2_ones(pu, lsum);
+          lsum[qb] = dot2_ones(pu, lsum[qb]);
           if (DROP) {
             const uint32_t keep =
-                (drop_keep(rnd[kb], r, drop.thr) ? 0xffffu : 0u) |
-                (drop_keep(rnd[kb], r + 1, drop.thr) ? 0xffff0000u : 0u);
+                (drop_keep(rnd[qb][kb], r, drop.thr) ? 0xffffu : 0u) |
+                (drop_keep(rnd[qb][kb], r + 1, drop.thr) ? 0xffff0000u : 0u);
             pv[qb][kb][s2][i] = pu & keep;
           } else {
             pv[qb][kb][s2][i] = pu;
           }
         }
-    l_run[qb] += lsum;
-  }
-
-  // O^T += V^T P^T: the V^T fragment is read once (transposing LDS load)
-  // and used for every query block.  A query block whose keys are all
-  // masked contributes p = 0.
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -156,6 +161,9 @@ __device__ __forceinline__ void fwd_tile(
           oacc[qb][cb] = mfma32(vf, __builtin_bit_cast(bf16x8, pv[qb][kb][s2]),
                                 oacc[qb][cb]);
       }
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) l_run[qb] += lsum[qb];
 }
 
 // Epilogue for one lane's query qi: O = o / l (0 for a row with no visible
