@@ -78,6 +78,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   // cores return dP - D (not with dropout, where D stays outside the mask).
   __shared__ __attribute__((aligned(16))) float LDs[2][2 * BR];
   __shared__ __attribute__((aligned(16))) float NDs[2][BR];
+  // lse2 by query (without dropout the interleaved pairs are not read: each
+  // lane fetches its 16 queries' lse2 and -D in eight 16-byte reads).
+  __shared__ __attribute__((aligned(16))) float LSs[2][BR];
 
   const int tid = threadIdx.x;
   // The wave index is uniform: readfirstlane lets the compiler see it, so
@@ -185,6 +188,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
       LDs[0][2 * tid] = l_nx;
       LDs[0][2 * tid + 1] = d_nx;
       NDs[0][tid] = -d_nx;
+      LSs[0][tid] = l_nx;
     }
   }
   wait_dma();
@@ -205,6 +209,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t *dOt = dOs[buf];
     const float *LDt = LDs[buf];
     const float *NDt = NDs[buf];
+    const float *LSt = LSs[buf];
 
 #pragma unroll
     for (int qb = 0; qb < BR / 32; ++qb) {
@@ -213,13 +218,18 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+      float lse_r[16];  // lse2 of register r's query (without dropout)
       if (!DROP) {  // dp starts at -D of register r's query
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x4 nd = *reinterpret_cast<const f32x4 *>(
-              &NDt[32 * qb + 16 * (j >> 1) + 8 * hh + 4 * (j & 1)]);
+          const int qo = 32 * qb + 16 * (j >> 1) + 8 * hh + 4 * (j & 1);
+          const f32x4 nd = *reinterpret_cast<const f32x4 *>(&NDt[qo]);
+          const f32x4 ls = *reinterpret_cast<const f32x4 *>(&LSt[qo]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dp[4 * j + e] = nd[e];
+          for (int e = 0; e < 4; ++e) {
+            dp[4 * j + e] = nd[e];
+            lse_r[4 * j + e] = ls[e];
+          }
         }
       }
 #pragma unroll
@@ -246,12 +256,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
           // registers 2i, 2i+1 hold two consecutive queries: one 16-byte
           // read gives both (lse2, D) pairs
           const int qo0 = 32 * qb + 16 * (i >> 2) + 8 * hh + 2 * (i & 3);
-          const f32x4 st = *reinterpret_cast<const f32x4 *>(&LDt[2 * qo0]);
+          f32x4 st;
+          if (DROP) st = *reinterpret_cast<const f32x4 *>(&LDt[2 * qo0]);
           float pv[2], dsv[2];
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const int r = 2 * i + t;
-            float p = fast_exp2(fmaf(s[r], c, -st[2 * t]));
+            const float lse = DROP ? st[2 * t] : lse_r[r];
+            float p = fast_exp2(fmaf(s[r], c, -lse));
             if (decltype(masked_tile)::value) {
               const bool masked =
                   key >= kv_valid || (CAUSAL && key > q0 + qo0 + t);
@@ -298,6 +310,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
       LDs[buf ^ 1][2 * tid] = l_nx;
       LDs[buf ^ 1][2 * tid + 1] = d_nx;
       NDs[buf ^ 1][tid] = -d_nx;
+      LSs[buf ^ 1][tid] = l_nx;
     }
     wait_dma();
     __syncthreads();
