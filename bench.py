@@ -207,16 +207,39 @@ def percentiles(ms):
             "p90": round(pick(0.9), 4)}
 
 
+# Untimed warm-up runs at least W calls and at least this long: the first
+# ~15 ms of steady GPU work measure up to 10% slower (clocks and caches
+# settle), which five steps of the 4K workload do not cover.
+MIN_WARM_S = 0.2
+
+
+def warm(fn, warmup):
+    """Calls fn(i) at least `warmup` times and until MIN_WARM_S of GPU work
+    has passed (synchronising every few calls so wall time tracks the GPU);
+    returns the number of calls."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < MIN_WARM_S:
+        fn(n)
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def time_step(attn, steps, warmup, backward=True, per_call=None):
     """Run warmup steps, then `steps` timed steps with events around each
     forward and backward call; returns mean ms of step, fwd and bwd (and,
     if per_call is a dict, fills it with each call's percentiles)."""
     torch = attn.torch
-    for _ in range(warmup):
+
+    def one(_):
         o, m, l = attn.fwd()
         if backward:
             attn.bwd(o, m, l)
-    torch.cuda.synchronize()
+    warm(one, warmup)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
           for _ in range(steps)]
     t0 = time.perf_counter()
@@ -284,11 +307,9 @@ def decode_bench(steps, warmup, splits=None, compare=True):
                      dtype=torch.uint8, device="cuda")
 
     def run(copies):
-        for i in range(warmup):
-            c = i % copies
-            fa.decode_paged(qd, kcs[c], vcs[c], table, lens, splits,
-                            workspace=ws)
-        torch.cuda.synchronize()
+        warm(lambda i: fa.decode_paged(qd, kcs[i % copies], vcs[i % copies],
+                                       table, lens, splits, workspace=ws),
+             warmup)
         e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
         e0.record()
         for i in range(steps):
@@ -340,9 +361,7 @@ def prefill_bench(steps, warmup):
     def call():
         return fa.prefill_paged(qd, kc, vc, table, lens, cud,
                                 w.seq_range[1], causal=True)
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
+    warm(lambda _: call(), warmup)
     e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
     e0.record()
     for _ in range(steps):
@@ -541,6 +560,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_s": MIN_WARM_S,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
