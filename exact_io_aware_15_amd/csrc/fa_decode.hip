@@ -251,16 +251,39 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
 
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+  // Partitions are read eight at a time with all of a chunk's loads in
+  // flight together (one memory latency per chunk rather than per
+  // partition); chunks are merged online, the running sums rescaled to each
+  // chunk's new max.  For up to eight partitions this is the plain merge:
+  // m = max_p m_p, w_p = exp(m_p - m), out = sum w_p o_p / sum w_p l_p.
+  constexpr int CH = 8;
   const int hq = blockIdx.x, b = blockIdx.y, col = threadIdx.x;
   const int S = a.num_splits;
   const size_t pbase = ((size_t)b * a.Hq + hq) * S;
-  float mx = a.part_m[pbase];
-  for (int s = 1; s < S; ++s) mx = fmaxf(mx, a.part_m[pbase + s]);
-  float acc = 0.f, lsum = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float w = fast_exp2((a.part_m[pbase + s] - mx) * a.c);
-    acc = fmaf(w, a.part_o[(pbase + s) * D + col], acc);
-    lsum = fmaf(w, a.part_l[pbase + s], lsum);
+  float mx = -INFINITY, acc = 0.f, lsum = 0.f;
+  for (int s0 = 0; s0 < S; s0 += CH) {
+    float pm[CH], pl[CH], po[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const bool ok = s0 + j < S;
+      const size_t p = pbase + s0 + j;
+      pm[j] = ok ? a.part_m[p] : -INFINITY;  // weight exp2(-inf) = 0
+      pl[j] = ok ? a.part_l[p] : 0.f;
+      po[j] = ok ? a.part_o[p * D + col] : 0.f;
+    }
+    float cm = mx;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) cm = fmaxf(cm, pm[j]);
+    const float r = fast_exp2((mx - cm) * a.c);  // 0 on the first chunk
+    acc *= r;
+    lsum *= r;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const float w = fast_exp2((pm[j] - cm) * a.c);
+      acc = fmaf(w, po[j], acc);
+      lsum = fmaf(w, pl[j], lsum);
+    }
+    mx = cm;
   }
   const float out = lsum > 0.f ? acc / lsum : 0.f;
   const __bf16 ob = (__bf16)out;
