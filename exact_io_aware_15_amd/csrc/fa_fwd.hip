@@ -75,9 +75,21 @@ __device__ __forceinline__ void fwd_tile(
   for (int qb = 0; qb < QB; ++qb) {
     const int qbase = qw + 32 * qb;
     const int qi = qbase + ln;
-    const bool need_mask =
-        (k0 + BC > kv_valid) || (CAUSAL && k0 + BC - 1 > qbase + qoff);
-    if (need_mask) {
+    const bool tail = k0 + BC > kv_valid;
+    const bool diag = CAUSAL && k0 + BC - 1 > qbase + qoff;
+    if (CAUSAL && diag && !tail) {
+      // Causal diagonal tile wholly inside kv_valid: register r's key is
+      // k0 + 8*hh + off(r) with off(r) a constant, so "key > qi + qoff" is
+      // one compare of that constant against a per-lane threshold.
+      const int thr_k = qi + qoff - k0 - 8 * hh;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = kb * 32 + 16 * (r >> 3) + (r & 7);
+          s[qb][kb][r] = off > thr_k ? -INFINITY : s[qb][kb][r];
+        }
+    } else if (tail || diag) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
