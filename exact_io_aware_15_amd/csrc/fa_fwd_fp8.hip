@@ -61,6 +61,28 @@ __device__ __forceinline__ void dma16(const uint8_t *src, uint8_t *dst) {
       (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
 }
 
+// Whole-tile fill through a raw buffer resource over the `bytes` bytes of a
+// slice at `base`: each wave issues SEGS/4 16-byte-per-lane loads at byte
+// offset off[u] (per lane) + tile_off (uniform) into its 1 KB segments.
+template <int SEGS>
+__device__ __forceinline__ void dma16_rows(uint8_t *tile, const uint8_t *base,
+                                           uint32_t bytes, uint32_t tile_off,
+                                           const uint32_t (&off)[SEGS / 4]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto src = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(base), (short)0, (int)bytes, 0x00020000);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t soff = __builtin_amdgcn_readfirstlane(tile_off);
+#pragma unroll
+  for (int u = 0; u < SEGS / 4; ++u)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src,
+        (__attribute__((address_space(3))) void *)(tile + (wave + 4 * u) *
+                                                              1024),
+        16, off[u], soff, 0, 0);
+#endif
+}
+
 __device__ __forceinline__ i32x8 cat8(u32x4 lo, u32x4 hi) {
   const i32x8 v = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                    (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
@@ -132,7 +154,6 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8FwdArgs a) {
   const float vd = a.v_descale ? a.v_descale[bh] : 1.0f;
   const float sscale = a.scale * qd * kd;  // natural units per raw score
   const float c = sscale * kLog2e;         // log2 units per raw score
-  const float thr = kRescaleLog2F8 / c;    // raw units
 
   const size_t hoff = (size_t)bh * N * D;
   const uint8_t *qg = a.q + hoff;
@@ -185,8 +206,19 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8FwdArgs a) {
     const int rv = p >> 2, pv = p & 3;
     voff[u] = (uint32_t)(rv * ldv + 16 * (pv ^ vt_swz(rv)));
   }
+  // Whole tiles go through buffer resources over the (b, h) slices (K:
+  // N*d <= 2^27 bytes; V^T: d*ldv bytes, used while that fits in 2^31), so
+  // a tile costs no vector address arithmetic.
+  const bool vt_buf = (size_t)D * ldv < ((size_t)1 << 31);
   auto load_tile = [&](int k0, int buf) {
     if (k0 + BC <= kv_valid && k0 + BC <= ldv) {
+      if (vt_buf) {
+        dma16_rows<SEGS>(Ks(buf), kg, (uint32_t)N * D, (uint32_t)k0 * D,
+                         koff);
+        dma16_rows<SEGS>(Vs(buf), vtg, (uint32_t)(D * ldv), (uint32_t)k0,
+                         voff);
+        return;
+      }
 #pragma unroll
       for (int u = 0; u < SEGS / 4; ++u) {
         const int seg = wave + 4 * u;
@@ -225,9 +257,18 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8FwdArgs a) {
           s[kb] = mfma_fp8(cat8(lo, hi), qf[mi], s[kb]);
         }
       }
-      const bool need_mask =
-          (k0 + BC > kv_valid) || (CAUSAL && k0 + BC - 1 > qw);
-      if (need_mask) {
+      const bool tail_keys = k0 + BC > kv_valid;
+      const bool diag = CAUSAL && k0 + BC - 1 > qw;
+      if (CAUSAL && diag && !tail_keys) {
+        // Causal diagonal tile inside kv_valid: register r's key is
+        // k0 + 16*hh + 32*kb + r, masked iff that offset exceeds qi - k0 - 16*hh.
+        const int thr_k = qi - k0 - 16 * hh;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[kb][r] = 32 * kb + r > thr_k ? -INFINITY : s[kb][r];
+      } else if (tail_keys || diag) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -237,15 +278,16 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(Fp8FwdArgs a) {
             s[kb][r] = masked ? -INFINITY : s[kb][r];
           }
       }
+      // A chain max(max(mx, a), b) per pair: one v_max3_f32 per two scores.
       float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2)
-          mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+          mx = fmaxf(fmaxf(mx, s[kb][r]), s[kb][r + 1]);
       mx = max_xor32(mx);
       m_max = fmaxf(m_max, mx);
-      if (__any(m_max - m_ref > thr)) {
+      if (__any((m_max - m_ref) * c > kRescaleLog2F8)) {
         asm volatile("" ::: "memory");
         const float alpha = fast_exp2((m_ref - m_max) * c);
         m_ref = m_max;
