@@ -235,10 +235,28 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
 
   // Query tiles in descending order (heaviest causal tiles first); heads vary
   // fastest, so workgroups dealt round-robin to the 8 XCDs keep one head's
-  // tiles on one XCD's L2 when B*H is a multiple of 8 (or divides 8).
+  // tiles on one XCD's L2 when B*H is a multiple of 8 (or divides 8).  With a
+  // paged cache the G query heads of one KV head read the same K/V tiles:
+  // their workgroups get block indices of equal residue mod 8 (one XCD, one
+  // L2).  Unit u = (query-tile rank, sequence, KV head), G heads each; the
+  // grid is rounded up to whole groups of eight units.
   const int nqt = (a.N + BR - 1) / BR;
-  const int bh = blockIdx.x % a.BH;
-  const int qt = nqt - 1 - (int)(blockIdx.x / a.BH);
+  int bh, qt;
+  if (PAGED) {
+    const int G = a.H / a.Hkv;
+    const int sx = (int)(blockIdx.x >> 3);
+    const int g = sx % G;
+    const int u = (sx / G) * 8 + (int)(blockIdx.x & 7);
+    const int BHk = a.B * a.Hkv;
+    if (u >= nqt * BHk) return;  // rounding of the grid
+    const int bhk = u % BHk;
+    qt = nqt - 1 - u / BHk;
+    const int bb = bhk / a.Hkv;
+    bh = bb * a.H + (bhk - bb * a.Hkv) * G + g;
+  } else {
+    bh = blockIdx.x % a.BH;
+    qt = nqt - 1 - (int)(blockIdx.x / a.BH);
+  }
   const int b = bh / a.H;
   const SliceRows sr = slice_rows(a.cu_seqlens, a.total, a.N, a.H, bh);
   const int N = sr.n;  // queries of this slice
@@ -572,8 +590,12 @@ hipError_t launch_fwd_block_sparse(const FwdArgs &a, int d, bool causal,
 
 hipError_t launch_prefill_paged(const FwdArgs &a, int d, bool causal,
                                 hipStream_t s) {
+  // Units of (query tile, sequence, KV head) in groups of eight, each unit's
+  // G = H / Hkv query heads on one XCD (see fwd_bf16_kernel).
   const int nqt = (a.N + 127) / 128;
-  dim3 grid((unsigned)(nqt * a.BH)), block(256);
+  const long long units = (long long)nqt * a.B * a.Hkv;
+  const long long blocks = 8LL * (a.H / a.Hkv) * ((units + 7) / 8);
+  dim3 grid((unsigned)blocks), block(256);
   if (d == 64) {
     if (causal)
       hipLaunchKernelGGL((fwd_bf16_kernel<64, 32, true, false, true>), grid,
