@@ -87,8 +87,12 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
   // per-wave conditions (diagonal tiles) become scalar branches.
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hh = lane >> 5;
-  const int bh = blockIdx.x % a.BH;
-  const int kt = blockIdx.x / a.BH;  // causal: low key tiles carry most work
+  // Causal: low key tiles carry most work; dealt so each CU's two resident
+  // workgroups (d = 64) carry equal work.
+  const int i = (CAUSAL && !SPARSE) ? causal_deal_order<D == 64 ? 2 : 1>(blockIdx.x)
+                                    : (int)blockIdx.x;
+  const int bh = i % a.BH;
+  const int kt = i / a.BH;
   const int b = bh / a.H;
   const SliceRows sr = slice_rows(a.cu_seqlens, a.total, a.N, a.H, bh);
   const int N = sr.n;
@@ -353,8 +357,12 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 31, hh = lane >> 5;
   const int nqt = (a.N + BR - 1) / BR;
-  const int bh = blockIdx.x % a.BH;
-  const int qt = nqt - 1 - (int)(blockIdx.x / a.BH);  // heaviest first
+  // Heaviest first, dealt so each CU's three resident workgroups (d = 64)
+  // carry equal work.
+  const int i = (CAUSAL && !SPARSE) ? causal_deal_order<D == 64 ? 3 : 1>(blockIdx.x)
+                                    : (int)blockIdx.x;
+  const int bh = i % a.BH;
+  const int qt = nqt - 1 - i / a.BH;
   const int b = bh / a.H;
   const SliceRows sr = slice_rows(a.cu_seqlens, a.total, a.N, a.H, bh);
   const int N = sr.n;

@@ -137,6 +137,28 @@ __device__ __forceinline__ SliceRows slice_rows(const int32_t *cu, int total,
   return {min(e - s, N), (size_t)h * total + s};
 }
 
+// Dispatch order of a causal grid whose blocks are sorted heaviest first.
+// The hardware deals a launch's blocks to the 8 XCDs in turn and, within an
+// XCD, to its 32 CUs in turn, so blocks i, i + 256, i + 512, ... are the
+// successive resident workgroups of one CU.  Reversing every odd round of
+// 256 blocks (in groups of eight, so each block keeps its XCD and a head its
+// L2) pairs the heaviest tiles of one round with the lightest of the next:
+// the ROUNDS rounds resident at once then carry about equal work on every
+// CU, instead of the CUs that hold the long causal rows finishing last.
+// Later rounds keep the heaviest-first order for the dynamic dispatch.  A
+// bijection on [0, grid) for any grid size (a partial last round is not
+// reversed).
+template <int ROUNDS>
+__device__ __forceinline__ int causal_deal_order(int i) {
+  constexpr int kRound = 256;
+  const int r = i / kRound;
+  if ((r & 1) && r < ROUNDS && (r + 1) * kRound <= (int)gridDim.x) {
+    const int p = i - r * kRound;
+    i = r * kRound + (kRound - 8 - (p & ~7)) + (p & 7);
+  }
+  return i;
+}
+
 __device__ __forceinline__ u32x4 ldg128(const void *p) {
   return *reinterpret_cast<const u32x4 *>(p);
 }

@@ -233,9 +233,10 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 31, hh = lane >> 5;
 
-  // Query tiles in descending order (heaviest causal tiles first); heads vary
-  // fastest, so workgroups dealt round-robin to the 8 XCDs keep one head's
-  // tiles on one XCD's L2 when B*H is a multiple of 8 (or divides 8).  With a
+  // Query tiles in descending order (heaviest causal tiles first, dealt so
+  // each CU's resident workgroups carry equal work); heads vary fastest, so
+  // workgroups dealt round-robin to the 8 XCDs keep one head's tiles on one
+  // XCD's L2 when B*H is a multiple of 8 (or divides 8).  With a
   // paged cache the G query heads of one KV head read the same K/V tiles:
   // their workgroups get block indices of equal residue mod 8 (one XCD, one
   // L2).  Unit u = (query-tile rank, sequence, KV head), G heads each; the
@@ -254,8 +255,13 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
     const int bb = bhk / a.Hkv;
     bh = bb * a.H + (bhk - bb * a.Hkv) * G + g;
   } else {
-    bh = blockIdx.x % a.BH;
-    qt = nqt - 1 - (int)(blockIdx.x / a.BH);
+    // Resident workgroups per CU: 4 (MINW = 4), 3 (other d = 64), 2 (d = 128).
+    const int i =
+        (CAUSAL && !SPARSE)
+            ? causal_deal_order<MINW == 4 ? 4 : (D == 64 ? 3 : 2)>(blockIdx.x)
+            : (int)blockIdx.x;
+    bh = i % a.BH;
+    qt = nqt - 1 - i / a.BH;
   }
   const int b = bh / a.H;
   const SliceRows sr = slice_rows(a.cu_seqlens, a.total, a.N, a.H, bh);
