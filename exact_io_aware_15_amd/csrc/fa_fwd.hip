@@ -501,12 +501,6 @@ __global__ __launch_bounds__(64, 1) void fwd_f32_kernel(FwdArgs a) {
   }
 }
 
-// Key ranges up to this length run the d = 64 forward at 4 waves per SIMD:
-// the extra resident workgroups hide more latency on short rows (measured
-// +7-9% at N = 1K and on the ragged prefill, neutral at 4K), while on long
-// rows the extra concurrent K/V streams per XCD cost L2 hits (-3% at 64K).
-constexpr int kFourWaveMaxN = 8192;
-
 template <int D, bool CAUSAL>
 hipError_t fwd_bf16_dispatch_pad(const FwdArgs &a, hipStream_t s) {
   // 32 queries per wave (one 32-query block), 4 waves per workgroup.
@@ -515,7 +509,11 @@ hipError_t fwd_bf16_dispatch_pad(const FwdArgs &a, hipStream_t s) {
   dim3 grid((unsigned)(nqt * a.BH)), block(256);
   const bool drop = a.drop.thr != 0;
   if constexpr (D == 64) {
-    if (!drop && a.N <= kFourWaveMaxN) {
+    // Without dropout the d = 64 forward runs 4 waves per SIMD (128 VGPRs):
+    // the extra resident workgroup per CU hides more latency (measured 1-9%
+    // faster than 3 waves from N = 1K to 64K once causal tiles are dealt
+    // evenly); the dropout forward needs more registers and keeps 3.
+    if (!drop) {
       if (a.kv_len)
         hipLaunchKernelGGL(
             (fwd_bf16_kernel<D, QPW, CAUSAL, true, false, false, false, 4>),
