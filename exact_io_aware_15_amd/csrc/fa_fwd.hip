@@ -245,9 +245,12 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
   int bh, qt;
   if (PAGED) {
     const int G = a.H / a.Hkv;
-    const int sx = (int)(blockIdx.x >> 3);
+    // Dealt like the dense grid (the deal keeps each block's residue mod 8).
+    const int bi = CAUSAL ? causal_deal_order<MINW == 4 ? 4 : (D == 64 ? 3 : 2)>(blockIdx.x)
+                          : (int)blockIdx.x;
+    const int sx = bi >> 3;
     const int g = sx % G;
-    const int u = (sx / G) * 8 + (int)(blockIdx.x & 7);
+    const int u = (sx / G) * 8 + (bi & 7);
     const int BHk = a.B * a.Hkv;
     if (u >= nqt * BHk) return;  // rounding of the grid
     const int bhk = u % BHk;
