@@ -138,11 +138,13 @@ __device__ __forceinline__ SliceRows slice_rows(const int32_t *cu, int total,
 }
 
 // Dispatch order of a causal grid whose blocks are sorted heaviest first.
-// The hardware deals a launch's blocks to the 8 XCDs in turn and, within an
-// XCD, to its 32 CUs in turn, so blocks i, i + 256, i + 512, ... are the
-// successive resident workgroups of one CU.  Reversing every odd round of
-// 256 blocks (in groups of eight, so each block keeps its XCD and a head its
-// L2) pairs the heaviest tiles of one round with the lightest of the next:
+// Model of the dispatcher this is built for: a launch's blocks go to the 8
+// XCDs in turn and, within an XCD, to its 32 CUs in turn, so blocks i,
+// i + 256, i + 512, ... become the successive resident workgroups of one CU
+// (the speed-ups measured with this order fit the model; results never
+// depend on it, since the order is a bijection).  Reversing every odd round
+// of 256 blocks (in groups of eight, so each block keeps its XCD and a head
+// its L2) pairs the heaviest tiles of one round with the lightest of the next:
 // the ROUNDS rounds resident at once then carry about equal work on every
 // CU, instead of the CUs that hold the long causal rows finishing last.
 // Later rounds keep the heaviest-first order for the dynamic dispatch.  A
