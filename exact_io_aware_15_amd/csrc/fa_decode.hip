@@ -10,8 +10,13 @@
 // parallelism along queries, so the key range is split over workgroups and
 // their (m, l, o) triples are merged (FA notes §3.1 merge rule).
 //
-// Split kernel: grid (Hkv, num_splits, B), NW waves.  Wave w of a split takes
-// the split's blocks w, w + NW, ...; their table entries sit one per lane.
+// Split kernel: grid (Hkv, num_splits, B), NW waves.  The G = Hq / Hkv query
+// heads of a group are MFMA columns 0 .. G-1 of a 16-column tile; GP >= G is
+// the group width the kernel is built for (a power of two, which sizes only
+// the LDS merge area), so every G <= 16 runs on the kernel of the next power
+// of two, the extra columns computing on zero queries and never stored.
+// Wave w of a split takes the split's blocks w, w + NW, ...; their table
+// entries sit one per lane.
 // Per block, on 16 x 16 matrix-core tiles (tokens x query heads of the
 // group): S^T = K Q^T with K read straight from HBM into registers, the
 // online-softmax update per head, then O^T += V^T P^T with V staged in LDS
@@ -62,19 +67,19 @@ __device__ __forceinline__ void dma_v_block(uint16_t *slot, const uint16_t *blk,
   }
 }
 
-template <int D, int G, int NW>
+template <int D, int GP, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   constexpr int TILE = kBlock * D;  // bf16 per V slot
   constexpr int KS = D / 32;        // k-steps of S^T = K Q^T
   constexpr int NC = D / 16;        // 16-row blocks of O^T
-  static_assert(G <= 16, "a query group must fit the 16 MFMA columns");
+  static_assert(GP <= 16, "a query group must fit the 16 MFMA columns");
   // One LDS object (the V slots, reused for the final merge), so that the
   // compiler does not make LDS reads wait for DMA into other slots.
   union Smem {
     uint16_t v[NW][2][TILE];
     struct {
-      float m[NW][G], l[NW][G];
-      float o[NW][G][D];
+      float m[NW][GP], l[NW][GP];
+      float o[NW][GP][D];
     } red;
   };
   __shared__ __attribute__((aligned(16))) Smem sm;
@@ -87,6 +92,7 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   const int col = lane & 15, grp = lane >> 4;  // MFMA column / lane group
   const int S = a.num_splits;
   const int Hkv = a.Hkv;
+  const int G = a.Hq / Hkv;  // 1 .. GP (validated by the caller)
 
   // Lengths beyond the table's capacity are clamped to it.
   const int len = min(max(a.seq_lens[b], 0), a.max_blocks * kBlock);
@@ -290,28 +296,28 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   a.out[((size_t)b * a.Hq + hq) * D + col] = __builtin_bit_cast(uint16_t, ob);
 }
 
-template <int D, int G>
+template <int D, int GP>
 hipError_t decode_dispatch_g(const DecodeArgs &a, hipStream_t s) {
   // Four waves per workgroup (32.5 KB of LDS at d = 128: four workgroups
   // per CU).
   constexpr int NW = 4;
-  hipLaunchKernelGGL((decode_split_kernel<D, G, NW>),
+  hipLaunchKernelGGL((decode_split_kernel<D, GP, NW>),
                      dim3(a.Hkv, a.num_splits, a.B), dim3(64 * NW), 0, s, a);
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.Hq, a.B), dim3(D), 0, s,
                      a);
   return hipGetLastError();
 }
 
+// Every group size 1 .. 16 (the caller rejects larger ones) runs on the
+// kernel built for the next power of two.
 template <int D>
 hipError_t decode_dispatch(const DecodeArgs &a, hipStream_t s) {
-  switch (a.Hq / a.Hkv) {
-    case 1: return decode_dispatch_g<D, 1>(a, s);
-    case 2: return decode_dispatch_g<D, 2>(a, s);
-    case 4: return decode_dispatch_g<D, 4>(a, s);
-    case 8: return decode_dispatch_g<D, 8>(a, s);
-    case 16: return decode_dispatch_g<D, 16>(a, s);
-    default: return hipErrorInvalidValue;
-  }
+  const int G = a.Hq / a.Hkv;
+  if (G <= 1) return decode_dispatch_g<D, 1>(a, s);
+  if (G <= 2) return decode_dispatch_g<D, 2>(a, s);
+  if (G <= 4) return decode_dispatch_g<D, 4>(a, s);
+  if (G <= 8) return decode_dispatch_g<D, 8>(a, s);
+  return decode_dispatch_g<D, 16>(a, s);
 }
 
 }  // namespace

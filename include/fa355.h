@@ -389,7 +389,10 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
  *
  *   B            sequences (>= 1).
  *   Hq, Hkv      query and KV heads; Hq % Hkv == 0, query head h reads KV head
- *                h / (Hq / Hkv); Hq / Hkv <= 16.
+ *                h / (Hq / Hkv).  Every group size Hq / Hkv from 1 to 16 is
+ *                supported (one that is not a power of two runs on the
+ *                kernel of the next power of two, its extra matrix columns
+ *                unused); above 16, FA_E_UNSUPPORTED.
  *   d            head dimension, 64 or 128.
  *   q            [B,Hq,d] bf16.
  *   k_cache,

@@ -15,8 +15,9 @@ variant reaches the plain definition of ``reference`` to rounding.
 * ``merge_triples`` / ``split_merge`` -- S12 exercise 1 (flash-decoding): keys
   split over workers, each keeps its own (m, l, o), and the triples merge with
   the FA notes §3.1 rule m = max(m1, m2), l = e^{m1-m} l1 + e^{m2-m} l2.
-* ``paged_online``   -- S12 "implement it": the same recurrence reading each
-  key tile through a block table.
+* ``paged_online``   -- S12 "implement it" (paged addressing): the block
+  table resolved to token rows, then ``online_rows`` with one cache block
+  per tile.
 
 The NaN guard (S12's box on exp(-inf - -inf)): with ``guard=False`` the running
 max starts at -inf, so a first tile that is entirely masked gives NaN; with
@@ -173,30 +174,27 @@ def split_merge(q, k, v, n_splits, tile=64, scale=None, causal=False,
     return np.divide(o, l[:, None], out=np.zeros_like(o), where=l[:, None] > 0)
 
 
-def paged_online(q, block_table, k_cache, v_cache, seq_len, block_size,
-                 scale=None):
-    """S12 "implement it" paged loop for one query vector q [d].
+def paged_online(q, k_cache, v_cache, table, length, scale=None):
+    """Decode of one query vector q [d] against one KV head's paged cache.
 
-    k_cache, v_cache: [num_blocks, block_size, d] (one KV head).  For each
-    logical block t with n = min(block_size, seq_len - t * block_size) > 0,
-    read the first n rows of physical block block_table[t] and apply the
-    running (m, l, o) update.  Returns o / l (0 for seq_len = 0).
+    Definition followed: S12 "implement it" (paged addressing): token p of
+    the sequence is slot p mod bs of physical block table[p // bs], with bs
+    the block size, so the last block is only partly filled.  Here the table
+    is first resolved into the flat cache row of each of the ``length``
+    tokens, and ``online_rows`` (the S12 recurrence, pinned on its own) then
+    runs over the gathered rows with tile = bs, i.e. one cache block per step
+    of the recurrence.
+
+    k_cache, v_cache: [num_blocks, bs, d] (one KV head).  Returns o / l
+    (zeros for length 0).
     """
+    n_blocks, bs, dv = v_cache.shape
     q = np.asarray(q, np.float64)
-    d = q.shape[-1]
-    sc = _scale(d, scale)
-    m, l, o = M_GUARD, 0.0, np.zeros(v_cache.shape[-1])
-    for t, phys in enumerate(block_table):
-        n = min(block_size, seq_len - t * block_size)
-        if n <= 0:
-            break
-        kb = np.asarray(k_cache[int(phys), :n], np.float64)
-        vb = np.asarray(v_cache[int(phys), :n], np.float64)
-        s = sc * (kb @ q)
-        m_new = max(m, s.max())
-        alpha = math.exp(m - m_new)
-        p = np.exp(s - m_new)
-        l = alpha * l + p.sum()
-        o = alpha * o + p @ vb
-        m = m_new
-    return o / l if l > 0 else o
+    if length <= 0:
+        return np.zeros(dv)
+    pos = np.arange(int(length))
+    flat = np.asarray(table, np.int64)[pos // bs] * bs + pos % bs
+    keys = np.asarray(k_cache, np.float64).reshape(n_blocks * bs, -1)[flat]
+    vals = np.asarray(v_cache, np.float64).reshape(n_blocks * bs, dv)[flat]
+    _, l, o = online_rows(q[None, :], keys, vals, bs, scale)
+    return o[0] / l[0] if l[0] > 0 else np.zeros(dv)

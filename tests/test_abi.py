@@ -130,6 +130,12 @@ def test_decode_workspace_and_validation(lib):
     assert call(splits=0) == -2
     assert call(scale=0.0) == -2
     assert call(Hq=64, Hkv=2) == -3      # group of 32 > 16
+    assert call(Hq=34, Hkv=2) == -3      # group of 17 > 16
+    # Groups that are not a power of two pass the group check: with a short
+    # workspace they stop at the workspace check (-4), not at -3.
+    for Hq, Hkv in ((24, 8), (40, 8), (48, 8), (30, 2), (15, 1)):
+        short = lib.fa_decode_workspace_bytes(16, Hq, 128, 8) - 4
+        assert call(Hq=Hq, Hkv=Hkv, ws_bytes=short) == -4, (Hq, Hkv)
     assert call(d=96) == -3
     assert call(bs=32) == -3
     assert call(ws_bytes=ws - 4) == -4

@@ -47,6 +47,11 @@ CASES = [  # (B, Hq, Hkv, d, lens)
     (2, 16, 2, 128, [100, 257]),
     (3, 32, 2, 64, [5, 64, 1000]),
     (2, 4, 1, 64, [16, 31]),
+    # group sizes that are not a power of two (run on the next one's kernel)
+    (3, 12, 4, 128, [1, 40, 333]),     # G = 3
+    (2, 10, 2, 128, [17, 250]),        # G = 5
+    (2, 12, 2, 64, [64, 129]),         # G = 6
+    (2, 12, 1, 128, [7, 300]),         # G = 12
 ]
 
 

@@ -1,7 +1,9 @@
 """GPU parity of fa_fwd_block_sparse / fa_bwd_block_sparse against the fp64
 block-sparse oracle: random masks with ragged last blocks, fully masked
-rows, causal and not, d = 64 and 128; an all-ones mask must reproduce the
-dense kernel bit for bit; the 16K workload is compared on sampled rows."""
+rows, causal and not, d = 64 and 128, masks wider than the kernels' 64-block
+ballot window (forward and full gradients); an all-ones mask must reproduce
+the dense kernel bit for bit; the 16K workload is compared on sampled
+rows."""
 
 import numpy as np
 import pytest
@@ -67,6 +69,58 @@ def test_block_sparse_fwd_bwd(B, H, N, d, causal, density, empty_row):
     assert_close("dq", dq, rq, BF16_TOL)
     assert_close("dk", dk, rk, BF16_TOL)
     assert_close("dv", dv, rv, BF16_TOL)
+
+
+# More than 64 mask blocks per row and column (N > 64 * 128): the mask walks
+# of the forward and dQ kernels (along a mask row) and of the dK/dV kernel
+# (down a mask column, stride nb) re-ballot when they cross from the first
+# 64-block window into the second.  Some rows and columns allow only blocks
+# of the second window, so a walk must skip the whole first window; one row
+# and one column allow nothing at all.
+WIDE = [  # (N, d, causal, density)
+    (8448, 64, False, 0.25),
+    (8448 + 37, 64, True, 0.5),
+    (8448, 128, True, 0.3),
+]
+
+
+def _wide_mask(N, density, seed):
+    nb = -(-N // 128)
+    assert nb > 64
+    m = _mask(1, N, density, seed)
+    m[0, 3, :] = 0
+    m[0, 3, 65] = 1            # row 3: only a block of the second window
+    m[0, :, 2] = 0
+    m[0, 64, 2] = m[0, 65, 2] = 1  # column 2: only second-window blocks
+    m[0, 10, :] = 0            # a row with no allowed block
+    m[0, :, 11] = 0            # a column with no allowed block
+    m[0, nb - 1, 0] = 1        # the last row reaches back to block 0
+    return m
+
+
+@pytest.mark.parametrize("N,d,causal,density", WIDE)
+def test_block_sparse_wider_than_one_ballot_window(N, d, causal, density):
+    seed = 5200 + N + d + causal
+    q, k, v = (normal((1, 1, N, d), seed, t, "bf16") for t in range(3))
+    do = normal((1, 1, N, d), seed, TID_DO, "bf16")
+    mask = _wide_mask(N, density, seed)
+    print(f"block-sparse wide N={N} d={d} causal={causal} "
+          f"blocks={mask.shape[1]} density={mask.mean():.2f}", flush=True)
+    (o, m, l), (dq, dk, dv) = _run(q, k, v, mask, causal, do)
+    ro, rm, rl = oracle.attention_fwd_block_sparse(q.exact, k.exact, v.exact,
+                                                   mask, 128, None, causal)
+    assert_close("wide.o", o, ro, BF16_TOL)
+    vis = np.isfinite(rm)
+    assert np.array_equal(np.isfinite(m), vis)
+    assert np.all(o[~vis] == 0) and np.all(l[~vis] == 0)
+    rq, rk, rv, _ = oracle.attention_bwd_block_sparse(
+        q.exact, k.exact, v.exact, do.exact, mask, 128, None, causal)
+    assert_close("wide.dq", dq, rq, BF16_TOL)
+    assert_close("wide.dk", dk, rk, BF16_TOL)
+    assert_close("wide.dv", dv, rv, BF16_TOL)
+    # keys of a column with no allowed block get exactly zero gradients
+    assert np.all(dk[0, 0, 11 * 128:12 * 128] == 0)
+    assert np.all(dv[0, 0, 11 * 128:12 * 128] == 0)
 
 
 def test_all_ones_mask_matches_dense_kernel_bitwise():

@@ -81,7 +81,9 @@ def test_paged_decode_invariant_to_block_placement():
 
 
 def test_paged_online_loop_equals_paged_definition():
-    """S12's paged recurrence (one query, one KV head) equals gather+softmax."""
+    """The paged recurrence (one query, one KV head; table resolved to token
+    rows, one block per tile) equals gather + softmax (the plain definition
+    in ``decode_paged``)."""
     rng = np.random.default_rng(22)
     lens = np.array([1, 16, 17, 100])
     cache = paged_cache(lens, 1, 8, 16, 7, cfg_seed=98)
@@ -89,9 +91,9 @@ def test_paged_online_loop_equals_paged_definition():
     ref = decode_paged(q, cache.k_cache.exact, cache.v_cache.exact,
                        cache.block_table, lens)
     for b in range(4):
-        o = paged_online(q[b, 0], cache.block_table[b],
-                         cache.k_cache.exact[:, 0],
-                         cache.v_cache.exact[:, 0], int(lens[b]), 16)
+        o = paged_online(q[b, 0], cache.k_cache.exact[:, 0],
+                         cache.v_cache.exact[:, 0], cache.block_table[b],
+                         int(lens[b]))
         assert np.max(np.abs(o - ref[b, 0])) <= 1e-13
 
 
