@@ -22,9 +22,8 @@ import math
 from ._lib import FA_BF16, FA_F32, FaError, LibraryMissing, check, lib
 
 __all__ = ["fwd", "bwd", "fwd_dropout", "bwd_dropout", "fwd_fp8",
-           "fwd_varlen",
-           "bwd_varlen", "fwd_block_sparse",
-           "bwd_block_sparse", "decode_paged",
+           "fwd_varlen", "bwd_varlen", "fwd_block_sparse",
+           "bwd_block_sparse", "decode_paged", "decode_paged_noalloc",
            "prefill_paged",
            "bwd_workspace_bytes", "bwd_varlen_workspace_bytes",
            "decode_workspace_bytes", "debug_flags", "CHECK_KV_LEN",
@@ -447,4 +446,36 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits=8,
                                    _ptr(workspace), workspace.numel(),
                                    _stream(q))
     check("fa_decode_paged", st)
+    return out
+
+
+def decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens,
+                         num_splits=8, scale=None, out=None):
+    """decode_paged through fa_decode_paged_noalloc: no workspace; the
+    partials live in the library's fixed per-GPU scratch (calls on one GPU
+    must not overlap).  `out` ([B,Hq,d] bf16) may be passed in, so that the
+    call allocates nothing."""
+    torch = _torch()
+    B, Hq, d = q.shape
+    nb, Hkv, bs, dk = k_cache.shape
+    _check_dev("q", q, torch.bfloat16)
+    _check_dev("k_cache", k_cache, torch.bfloat16)
+    _check_dev("v_cache", v_cache, torch.bfloat16, k_cache.shape)
+    if dk != d:
+        raise ValueError("k_cache head dim differs from q")
+    _check_dev("block_table", block_table, torch.int32)
+    _check_dev("seq_lens", seq_lens, torch.int32, (B,))
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_dev("out", out, torch.bfloat16, q.shape)
+    with torch.cuda.device(q.device):
+        st = lib().fa_decode_paged_noalloc(
+            B, Hq, Hkv, d, _ptr(q), _ptr(k_cache), _ptr(v_cache), nb, bs,
+            _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+            num_splits, scale, _ptr(out), _stream(q))
+    check("fa_decode_paged_noalloc", st)
     return out

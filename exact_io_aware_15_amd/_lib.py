@@ -18,7 +18,9 @@ LIB_PATH = (DEBUG_LIB_PATH if os.environ.get("FA355_DEBUG", "0") not in
 
 FA_F32, FA_BF16 = 0, 1
 STATUS = {0: "FA_OK", -1: "FA_E_NULLPTR", -2: "FA_E_SHAPE",
-          -3: "FA_E_UNSUPPORTED", -4: "FA_E_WORKSPACE", -5: "FA_E_HIP"}
+          -3: "FA_E_UNSUPPORTED", -4: "FA_E_WORKSPACE", -5: "FA_E_HIP",
+          -6: "FA_E_SCRATCH"}
+FA_DECODE_SCRATCH_BYTES = 8 << 20
 
 # Every function the header declares, with its ctypes signature.
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -53,6 +55,8 @@ SIGNATURES = {
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "fa_decode_paged": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P,
                              _I, _F, _P, _P, _Z, _P]),
+    "fa_decode_paged_noalloc": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _I, _P,
+                                     _I, _P, _I, _F, _P, _P]),
 }
 
 

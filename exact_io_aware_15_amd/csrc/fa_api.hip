@@ -4,6 +4,8 @@
 // call returns its status with no side effect (also on a machine with no GPU).
 #include <math.h>
 
+#include <mutex>
+
 #include "fa355.h"
 #include "fa_kernels.h"
 
@@ -108,6 +110,100 @@ int bwd_dense(int B, int H, int N, int d, const void *q, const void *k,
   return from_hip(launch_bwd(a, d, causal != 0, s));
 }
 
+size_t fa_decode_workspace_bytes_impl(int B, int Hq, int d, int num_splits) {
+  if (B < 1 || Hq < 1 || (d != 64 && d != 128) || num_splits < 1 ||
+      num_splits > 64)
+    return 0;
+  const size_t parts = (size_t)B * Hq * num_splits;
+  return 2 * align_up(parts * sizeof(float)) +
+         align_up(parts * d * sizeof(float));
+}
+
+// Arguments of a paged decode, checked without touching the device.
+int decode_validate(int B, int Hq, int Hkv, int d, const void *q,
+                    const void *k_cache, const void *v_cache, int num_blocks,
+                    int block_size, const int32_t *block_table,
+                    int max_blocks_per_seq, const int32_t *seq_lens,
+                    int num_splits, float scale, const void *out) {
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
+    return FA_E_NULLPTR;
+  if (B < 1 || Hq < 1 || Hkv < 1 || num_blocks < 1 ||
+      max_blocks_per_seq < 1 || num_splits < 1 || num_splits > 64 ||
+      !valid_scale(scale))
+    return FA_E_SHAPE;
+  if (Hq % Hkv != 0) return FA_E_SHAPE;
+  if (Hq / Hkv > 16) return FA_E_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
+  if (block_size != 16) return FA_E_UNSUPPORTED;
+  if ((long long)B * max_blocks_per_seq > (1LL << 31) - 1 ||
+      (long long)max_blocks_per_seq * 16 > (1LL << 31) - 1 ||
+      (long long)num_blocks * block_size * Hkv * d > (1LL << 40))
+    return FA_E_SHAPE;
+  return FA_OK;
+}
+
+// Enqueues a validated decode whose partial triples live at ws (laid out as
+// fa_decode_workspace_bytes counts them).
+int decode_launch(int B, int Hq, int Hkv, int d, const void *q,
+                  const void *k_cache, const void *v_cache, int num_blocks,
+                  int block_size, const int32_t *block_table,
+                  int max_blocks_per_seq, const int32_t *seq_lens,
+                  int num_splits, float scale, void *out, char *ws,
+                  void *stream) {
+  const size_t parts = (size_t)B * Hq * num_splits;
+  DecodeArgs a{};
+  a.q = (const uint16_t *)q;
+  a.k_cache = (const uint16_t *)k_cache;
+  a.v_cache = (const uint16_t *)v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = (uint16_t *)out;
+  a.part_m = (float *)ws;
+  a.part_l = (float *)(ws + align_up(parts * sizeof(float)));
+  a.part_o = (float *)(ws + 2 * align_up(parts * sizeof(float)));
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.num_splits = num_splits;
+  a.scale = scale;
+  a.c = (float)((double)scale * 1.4426950408889634);
+  hipStream_t s = (hipStream_t)stream;
+  if (kChecks)
+    if (hipError_t e = check_paged(seq_lens, nullptr, block_table, B,
+                                   max_blocks_per_seq, block_size, num_blocks,
+                                   s))
+      return from_hip(e);
+  return from_hip(launch_decode(a, d, s));
+}
+
+// Fixed scratch of fa_decode_paged_noalloc: one array per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never
+// the device memory: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, called once per device with that device current, and
+// only that address is handed to kernels.  The split kernel writes every
+// partial triple of a call before the merge kernel reads it, so nothing in
+// the array has to start at zero.
+constexpr size_t kScratchBytes = FA_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+char *scratch_dev[kMaxDevices];  // device address per device, once known
+
+int scratch_on_current_device(char **ptr) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev)) return from_hip(e);
+  if (dev < 0 || dev >= kMaxDevices) return FA_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (scratch_dev[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)))
+      return from_hip(e);
+    scratch_dev[dev] = (char *)p;
+  }
+  *ptr = scratch_dev[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,6 +216,8 @@ const char *fa_status_str(int status) {
     case FA_E_UNSUPPORTED: return "FA_E_UNSUPPORTED: not implemented in this build";
     case FA_E_WORKSPACE: return "FA_E_WORKSPACE: workspace missing or too small";
     case FA_E_HIP: return "FA_E_HIP: HIP runtime error at launch";
+    case FA_E_SCRATCH:
+      return "FA_E_SCRATCH: request larger than the library's fixed scratch";
     default: return "unknown fa_status";
   }
 }
@@ -386,12 +484,7 @@ int fa_prefill_paged(int B, int Hq, int Hkv, int d, int total_q, int max_q,
 }
 
 size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
-  if (B < 1 || Hq < 1 || (d != 64 && d != 128) || num_splits < 1 ||
-      num_splits > 64)
-    return 0;
-  const size_t parts = (size_t)B * Hq * num_splits;
-  return 2 * align_up(parts * sizeof(float)) +
-         align_up(parts * d * sizeof(float));
+  return fa_decode_workspace_bytes_impl(B, Hq, d, num_splits);
 }
 
 int fa_decode_paged(int B, int Hq, int Hkv, int d, const void *q,
@@ -400,47 +493,36 @@ int fa_decode_paged(int B, int Hq, int Hkv, int d, const void *q,
                     int max_blocks_per_seq, const int32_t *seq_lens,
                     int num_splits, float scale, void *out, void *workspace,
                     size_t workspace_bytes, void *stream) {
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
-    return FA_E_NULLPTR;
-  if (B < 1 || Hq < 1 || Hkv < 1 || num_blocks < 1 ||
-      max_blocks_per_seq < 1 || num_splits < 1 || num_splits > 64 ||
-      !valid_scale(scale))
-    return FA_E_SHAPE;
-  if (Hq % Hkv != 0) return FA_E_SHAPE;
-  if (Hq / Hkv > 16) return FA_E_UNSUPPORTED;
-  if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
-  if (block_size != 16) return FA_E_UNSUPPORTED;
-  if ((long long)B * max_blocks_per_seq > (1LL << 31) - 1 ||
-      (long long)max_blocks_per_seq * 16 > (1LL << 31) - 1 ||
-      (long long)num_blocks * block_size * Hkv * d > (1LL << 40))
-    return FA_E_SHAPE;
+  if (int st = decode_validate(B, Hq, Hkv, d, q, k_cache, v_cache, num_blocks,
+                               block_size, block_table, max_blocks_per_seq,
+                               seq_lens, num_splits, scale, out))
+    return st;
   const size_t need = fa_decode_workspace_bytes(B, Hq, d, num_splits);
   if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
   if (((uintptr_t)workspace) % kAlign) return FA_E_WORKSPACE;
-  const size_t parts = (size_t)B * Hq * num_splits;
-  DecodeArgs a{};
-  a.q = (const uint16_t *)q;
-  a.k_cache = (const uint16_t *)k_cache;
-  a.v_cache = (const uint16_t *)v_cache;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.out = (uint16_t *)out;
-  char *ws = (char *)workspace;
-  a.part_m = (float *)ws;
-  a.part_l = (float *)(ws + align_up(parts * sizeof(float)));
-  a.part_o = (float *)(ws + 2 * align_up(parts * sizeof(float)));
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_blocks = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.num_splits = num_splits;
-  a.scale = scale;
-  a.c = (float)((double)scale * 1.4426950408889634);
-  hipStream_t s = (hipStream_t)stream;
-  if (kChecks)
-    if (hipError_t e = check_paged(seq_lens, nullptr, block_table, B,
-                                   max_blocks_per_seq, block_size, num_blocks,
-                                   s))
-      return from_hip(e);
-  return from_hip(launch_decode(a, d, s));
+  return decode_launch(B, Hq, Hkv, d, q, k_cache, v_cache, num_blocks,
+                       block_size, block_table, max_blocks_per_seq, seq_lens,
+                       num_splits, scale, out, (char *)workspace, stream);
+}
+
+int fa_decode_paged_noalloc(int B, int Hq, int Hkv, int d, const void *q,
+                            const void *k_cache, const void *v_cache,
+                            int num_blocks, int block_size,
+                            const int32_t *block_table,
+                            int max_blocks_per_seq, const int32_t *seq_lens,
+                            int num_splits, float scale, void *out,
+                            void *stream) {
+  if (int st = decode_validate(B, Hq, Hkv, d, q, k_cache, v_cache, num_blocks,
+                               block_size, block_table, max_blocks_per_seq,
+                               seq_lens, num_splits, scale, out))
+    return st;
+  if (fa_decode_workspace_bytes(B, Hq, d, num_splits) > kScratchBytes)
+    return FA_E_SCRATCH;
+  char *ws = nullptr;
+  if (int st = scratch_on_current_device(&ws)) return st;
+  return decode_launch(B, Hq, Hkv, d, q, k_cache, v_cache, num_blocks,
+                       block_size, block_table, max_blocks_per_seq, seq_lens,
+                       num_splits, scale, out, ws, stream);
 }
 
 int fa_debug_flags(uint32_t *flags, int clear) {

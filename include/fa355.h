@@ -9,7 +9,9 @@
  *
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
- *     allocates, frees and caches nothing, and keeps no state between calls.
+ *     allocates, frees and caches nothing, and keeps no state between calls
+ *     (one exception: fa_decode_paged_noalloc uses a fixed device array that
+ *     the library itself holds, see there).
  *   - Every call only enqueues work on `stream` (a hipStream_t passed as void*;
  *     NULL means the null stream) and returns without synchronising.  Calls are
  *     reentrant; calls that share output or workspace buffers must be ordered
@@ -44,7 +46,8 @@ typedef enum {
   FA_E_SHAPE = -2,       /* a size is out of range or inconsistent             */
   FA_E_UNSUPPORTED = -3, /* valid request this build does not implement        */
   FA_E_WORKSPACE = -4,   /* workspace missing or smaller than the query says   */
-  FA_E_HIP = -5          /* the HIP runtime reported an error at launch        */
+  FA_E_HIP = -5,         /* the HIP runtime reported an error at launch        */
+  FA_E_SCRATCH = -6      /* request larger than the library's fixed scratch    */
 } fa_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -423,6 +426,38 @@ int fa_decode_paged(int B, int Hq, int Hkv, int d,
                     const int32_t *seq_lens, int num_splits, float scale,
                     void *out, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * fa_decode_paged_noalloc -- fa_decode_paged for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments, kernels and results (bitwise),
+ * without the workspace.  The per-split partial triples live instead in a
+ * fixed array of FA_DECODE_SCRATCH_BYTES bytes that the library holds on
+ * each GPU it runs on until the process ends.  The call itself allocates
+ * nothing: no hipMalloc, hipFree or allocating library routine.
+ *
+ *   Limit     fa_decode_workspace_bytes(B, Hq, d, num_splits) must not exceed
+ *             FA_DECODE_SCRATCH_BYTES (8 MiB: e.g. B * Hq * num_splits up to
+ *             16,128 at d = 128), else FA_E_SCRATCH, touching nothing.
+ *   Sharing   every call on one GPU uses that GPU's one array.  Calls that
+ *             may overlap on one GPU (other streams, other threads, other
+ *             processes' contexts excepted) race and must be ordered by the
+ *             caller, e.g. by issuing them on one stream.  The array keeps
+ *             the last call's partials; nothing in it needs to start at zero,
+ *             since each call writes every partial it reads.
+ *   Set-up    the first call on a device (with that device current) looks up
+ *             the device address of that GPU's copy of the array; a failure
+ *             there returns FA_E_HIP.
+ * Other arguments and errors: as fa_decode_paged.
+ */
+#define FA_DECODE_SCRATCH_BYTES ((size_t)8 << 20)
+int fa_decode_paged_noalloc(int B, int Hq, int Hkv, int d,
+                            const void *q, const void *k_cache,
+                            const void *v_cache, int num_blocks,
+                            int block_size, const int32_t *block_table,
+                            int max_blocks_per_seq, const int32_t *seq_lens,
+                            int num_splits, float scale, void *out,
+                            void *stream);
 
 #ifdef __cplusplus
 }

@@ -139,6 +139,18 @@ def test_decode_workspace_and_validation(lib):
     assert call(d=96) == -3
     assert call(bs=32) == -3
     assert call(ws_bytes=ws - 4) == -4
+    # the no-allocation variant validates the same way, and rejects a
+    # request its fixed scratch cannot hold before touching the device
+    def call_na(Hq=32, Hkv=8, d=128, splits=8, B=16, q=FAKE):
+        return lib.fa_decode_paged_noalloc(B, Hq, Hkv, d, q, FAKE, FAKE, 100,
+                                           16, FAKE, 512, FAKE, splits, 0.1,
+                                           FAKE, NULL)
+    assert call_na(q=NULL) == -1
+    assert call_na(Hkv=7) == -2
+    assert call_na(Hq=64, Hkv=2) == -3
+    assert lib.fa_decode_workspace_bytes(64, 64, 128, 8) > \
+        _lib.FA_DECODE_SCRATCH_BYTES
+    assert call_na(B=64, Hq=64) == -6
     # a capacity of max_blocks_per_seq * 16 tokens must fit an int
     assert lib.fa_decode_paged(1, 32, 8, 128, FAKE, FAKE, FAKE, 100, 16, FAKE,
                                1 << 27, FAKE, 8, 0.1, FAKE, FAKE, ws,
