@@ -89,14 +89,48 @@ def compulsory_bytes(w, backward):
 LDS_BYTES_PER_CU = 160 * 1024
 
 
+def strip_c_comments(text):
+    """C/C++ source without its comments (// and /* */ outside string and
+    character literals), each comment replaced by one space, and every run
+    of whitespace collapsed to one space: what the compiler sees as tokens."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                       # literal: copy through its end
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash():
-    """Hash of the kernel sources: counters are valid only for this hash."""
+    """Hash of what the kernels are built from: the comment-stripped,
+    whitespace-normalised sources under csrc/ and the compiler flags.  The
+    committed counter summaries are valid only for this hash (a comment edit
+    leaves it unchanged; any code or flag change does not)."""
+    from exact_io_aware_15_amd import build as fa_build
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_io_aware_15_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(strip_c_comments(f.read()).encode())
+    flags = [f for f in fa_build.FLAGS + fa_build.KERNEL_FLAGS
+             if not os.path.isabs(f)]       # include paths vary by checkout
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 

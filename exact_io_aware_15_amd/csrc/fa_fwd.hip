@@ -510,41 +510,31 @@ hipError_t fwd_bf16_dispatch_pad(const FwdArgs &a, hipStream_t s) {
   constexpr int QPW = 32;
   const int nqt = (a.N + 4 * QPW - 1) / (4 * QPW);
   dim3 grid((unsigned)(nqt * a.BH)), block(256);
-  const bool drop = a.drop.thr != 0;
-  if constexpr (D == 64) {
-    // Without dropout the d = 64 forward runs 4 waves per SIMD (128 VGPRs):
-    // the extra resident workgroup per CU hides more latency (measured 1-9%
-    // faster than 3 waves from N = 1K to 64K once causal tiles are dealt
-    // evenly); the dropout forward needs more registers and keeps 3.
-    if (!drop) {
-      if (a.kv_len)
-        hipLaunchKernelGGL(
-            (fwd_bf16_kernel<D, QPW, CAUSAL, true, false, false, false, 4>),
-            grid, block, 0, s, a);
-      else
-        hipLaunchKernelGGL(
-            (fwd_bf16_kernel<D, QPW, CAUSAL, false, false, false, false, 4>),
-            grid, block, 0, s, a);
-      return hipGetLastError();
-    }
-  }
-  if (a.kv_len) {
-    if (drop)
+  if (a.drop.thr != 0) {
+    // Dropout needs more registers (three waves per SIMD at d = 64).
+    if (a.kv_len)
       hipLaunchKernelGGL(
           (fwd_bf16_kernel<D, QPW, CAUSAL, true, false, false, true>), grid,
           block, 0, s, a);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, QPW, CAUSAL, true>), grid, block,
-                         0, s, a);
-  } else {
-    if (drop)
       hipLaunchKernelGGL(
           (fwd_bf16_kernel<D, QPW, CAUSAL, false, false, false, true>), grid,
           block, 0, s, a);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, QPW, CAUSAL, false>), grid, block,
-                         0, s, a);
+    return hipGetLastError();
   }
+  // Without dropout the d = 64 forward runs 4 waves per SIMD (128 VGPRs):
+  // the extra resident workgroup per CU hides more latency (measured 1-9%
+  // faster than 3 waves from N = 1K to 64K once causal tiles are dealt
+  // evenly); d = 128 needs more registers and runs 2.
+  constexpr int MINW = D == 64 ? 4 : 2;
+  if (a.kv_len)
+    hipLaunchKernelGGL(
+        (fwd_bf16_kernel<D, QPW, CAUSAL, true, false, false, false, MINW>),
+        grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(
+        (fwd_bf16_kernel<D, QPW, CAUSAL, false, false, false, false, MINW>),
+        grid, block, 0, s, a);
   return hipGetLastError();
 }
 

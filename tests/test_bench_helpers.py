@@ -57,3 +57,16 @@ def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_source_hash_ignores_comments_and_layout_only():
+    a = "int f(int x) {  // first comment\n  return x + 1;  /* two */ }\n"
+    b = "/* other words */ int f(int x) {\n\treturn x + 1; // changed\n}"
+    c = "int f(int x) { return x + 2; }"
+    assert bench.strip_c_comments(a) == bench.strip_c_comments(b)
+    assert bench.strip_c_comments(a) != bench.strip_c_comments(c)
+    # comment markers inside literals are code, not comments
+    assert bench.strip_c_comments('s = "a // b"; t = \'/\';') == \
+        's = "a // b"; t = \'/\';'
+    h = bench.source_hash()
+    assert len(h) == 16 and h == bench.source_hash()

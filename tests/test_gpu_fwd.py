@@ -158,15 +158,17 @@ def test_fwd_workload_sampled_rows(name):
     _check(name, q, k, v, w.causal, None, BF16_TOL, rows=rows)
 
 
-# d = 64 rows up to 8192 keys run at four waves per SIMD, longer ones at
-# three: both sides of the switch, padded and not, on sampled rows.
+# Long d = 64 rows with ragged tails (N not a multiple of the 128-query or
+# 64-key tile), padded and not, causal and not, on sampled rows: a partial
+# last query tile, a partial last key tile, and key padding that ends inside
+# a tile, all at lengths where the causal deal order reverses whole rounds.
 @pytest.mark.parametrize("N,causal,kv_len", [
     (8192, True, [8192, 5000]),
     (8193, True, None),
     (8257, False, [8257, 7000]),
     (8257, True, [3000, 8200]),
 ])
-def test_fwd_d64_either_side_of_the_occupancy_switch(N, causal, kv_len):
+def test_fwd_d64_long_rows_ragged_tails_and_padding(N, causal, kv_len):
     B, H, d = 2, 1, 64
     q, k, v = (normal((B, H, N, d), 9600 + N, t, "bf16") for t in range(3))
     rows = np.unique(np.concatenate([[0, 1, 127, 128, 2999, 3000, 4999, 5000,
