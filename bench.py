@@ -78,7 +78,7 @@ def compulsory_bytes(w, backward):
     """Bytes every implementation must move: inputs read once, outputs
     written once (fwd: Q,K,V in, O out, m,l out; bwd: Q,K,V,O,dO in,
     dQ,dK,dV out, m,l in)."""
-    s = 2 if w.dtype == "bf16" else 4
+    s = 2 if w.dtype == "bf16" else (1 if w.dtype == "fp8" else 4)
     nd = w.B * w.H * w.N * w.d
     rows = w.B * w.H * w.N
     if backward:
@@ -87,6 +87,28 @@ def compulsory_bytes(w, backward):
 
 
 LDS_BYTES_PER_CU = 160 * 1024
+THETA_M_ELEMENTS = LDS_BYTES_PER_CU // 2   # on-chip memory M in bf16 elements
+QUERY_TILE = 128                           # queries per forward workgroup
+
+
+def io_block(w, measured):
+    """Bytes per forward call: measured (rocprofv3 counters, or None),
+    compulsory (every input read once, every output written once), the
+    Theta(N^2 d^2 / M) bound of FA notes §3.5 (constants dropped, M = one
+    CU's LDS in elements), and the tile-reload model: Q read and O written
+    once, all of K and V read once per 128-query tile (half of them under
+    the causal mask), i.e. what HBM would see with no cache reuse across
+    query tiles.  Halving follows the causal mask's half of the score
+    matrix."""
+    s = 2 if w.dtype == "bf16" else (1 if w.dtype == "fp8" else 4)
+    bh, nd = w.B * w.H, w.N * w.d
+    half = 0.5 if w.causal else 1.0
+    tiles = -(-w.N // QUERY_TILE)
+    return {"unit": "bytes per call", "measured": measured,
+            "compulsory": compulsory_bytes(w, False),
+            "theta_bound": s * bh * flash_accesses(w.N, w.d,
+                                                   THETA_M_ELEMENTS) * half,
+            "tile_reload_model": s * bh * (2 * nd + 2 * nd * tiles * half)}
 
 
 def strip_c_comments(text):
@@ -152,7 +174,10 @@ def parse():
                          "single-copy decode): for profiling runs, so that "
                          "every traced dispatch is one the reported rates "
                          "count")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-probe", action="store_true",
+                    help="skip the machine probes (matrix-core loop rate, "
+                         "clock under load, streaming read rate)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device-to-device copy of this many "
                          "bytes --steps times (the reference reading that "
@@ -429,6 +454,14 @@ def sweep_one(name, steps, warmup, out):
         r["bwd_ms"] = round(bwd_ms, 4)
         r["bwd_tflops"] = round(w.bwd_flops() / bwd_ms / 1e9, 1)
         r["bwd_frac"] = round(r["bwd_tflops"] / PEAK_BF16_TFLOPS, 4)
+    eff = effective_fraction(w)
+    if eff is not None:   # key padding: FLOPs of the valid (query, key) pairs
+        r["valid_pair_fraction"] = round(eff, 4)
+        r["fwd_tflops_effective"] = round(r["fwd_tflops"] * eff, 1)
+        if w.backward:
+            r["bwd_tflops_effective"] = round(r["bwd_tflops"] * eff, 1)
+    if w.kind == "attn":
+        r["io"] = io_block(w, traffic_for(f"fa_fwd:{name}"))
     if w.kind == "fp8":   # against the bf16 forward of the same shape
         r["fwd_frac_of_fp8_peak"] = round(r["fwd_tflops"] / PEAK_FP8_TFLOPS,
                                           4)
@@ -455,6 +488,16 @@ def sweep_one(name, steps, warmup, out):
     out[name] = r
     del attn
     return r
+
+
+def effective_fraction(w):
+    """Share of the nominal N x N (query, key) pairs that key padding leaves
+    valid (None without padding): sum_b N * kv_len_b / (B * N^2)."""
+    import numpy as np
+    kl = w.kv_len() if w.kind == "attn" else None
+    if kl is None:
+        return None
+    return float(np.sum(np.asarray(kl, np.float64))) / (w.B * w.N)
 
 
 def sweep(steps, warmup):
@@ -496,10 +539,121 @@ def cpu_baseline(w, budget_s):
         el = time.perf_counter() - t0
         if el >= budget_s or heads >= w.B * w.H:
             break
+    blas, _ = _blas_info()
     return {"value": round(per_head * heads / el / 1e12, 6),
             "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"fp64 oracle fwd+bwd on {heads} of {w.B * w.H} heads "
-                      f"of {w.name} ({el:.1f} s)"}
+                      f"of {w.name} ({el:.1f} s)",
+            "os_cpu_count": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "blas": blas}
+
+
+def _blas_info():
+    """Name and thread count of the BLAS numpy uses."""
+    import numpy as np
+    name = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        name = cfg.get("Build Dependencies", {}).get("blas", {}).get("name")
+    except Exception:
+        pass
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        pass
+    return name, threads
+
+
+def _visible_pairs(rows, n_keys, causal, kv):
+    """(query, key) pairs the rows see: keys < kv, and <= the row if causal."""
+    import numpy as np
+    rows = np.asarray(rows, np.int64)
+    vis = np.full(rows.shape, min(kv, n_keys), np.int64)
+    if causal:
+        vis = np.minimum(vis, rows + 1)
+    return int(vis.sum())
+
+
+def cpu_baseline_configs(budget_s):
+    """The fp64 oracle on a bounded sample of every configuration: the
+    forward of each attention workload on one head's leading rows (rows
+    added until about budget_s / 8 seconds; causal rows see their prefix),
+    the backward of the three fwd+bwd workloads on one whole head, and the
+    paged decode on its first sequences.  Rates use the algorithmic counts
+    of the sample (4 d FLOP per visible pair forward, 10 d backward; K and
+    V bytes read for the decode)."""
+    import numpy as np
+    import oracle
+    from workloads import WORKLOADS
+    per = budget_s / 8
+    out = {}
+    for name in ("tiny_f32", "bert_large_padded", "gpt2_medium_causal_1k",
+                 "gpt2_medium_causal_4k", "long_causal_16k_d128",
+                 "long_causal_64k_d64"):
+        w = WORKLOADS[name]
+        q, k, v = w.qkv()
+        kl = w.kv_len()
+        kv = w.N if kl is None else int(kl[0])
+        sl = (slice(0, 1), slice(0, 1))
+        klb = None if kl is None else kl[0:1]
+        t0, n, pairs = time.perf_counter(), 0, 0
+        step = min(w.N, 256)
+        while n < w.N:
+            rows = np.arange(n, min(w.N, n + step))
+            oracle.attention_fwd(q.exact[sl], k.exact[sl], v.exact[sl], None,
+                                 w.causal, klb, rows=rows)
+            pairs += _visible_pairs(rows, w.N, w.causal, kv)
+            n += rows.size
+            if time.perf_counter() - t0 >= per:
+                break
+        el = time.perf_counter() - t0
+        e = {"fwd_tflops": round(4 * w.d * pairs / el / 1e12, 6),
+             "fwd_sample": f"head 0, rows 0..{n - 1} of {w.N} "
+                           f"({el:.2f} s)"}
+        if w.backward:
+            do = w.dout()
+            t0 = time.perf_counter()
+            oracle.attention_bwd(q.exact[sl], k.exact[sl], v.exact[sl],
+                                 do.exact[sl], None, w.causal, klb)
+            el = time.perf_counter() - t0
+            allp = _visible_pairs(np.arange(w.N), w.N, w.causal, kv)
+            e["bwd_tflops"] = round(10 * w.d * allp / el / 1e12, 6)
+            e["bwd_sample"] = f"head 0, all {w.N} rows ({el:.2f} s)"
+        out[name] = e
+    w = WORKLOADS["paged_gqa_decode"]
+    q, cache = w.decode_inputs(poison_tails=False)
+    t0, nb = time.perf_counter(), 0
+    kv_bytes = 0
+    while nb < w.B and time.perf_counter() - t0 < per:
+        oracle.decode_paged(q.exact[nb:nb + 1], cache.k_cache.exact,
+                            cache.v_cache.exact, cache.block_table[nb:nb + 1],
+                            cache.seq_lens[nb:nb + 1])
+        kv_bytes += int(cache.seq_lens[nb]) * w.Hkv * w.d * 2 * 2
+        nb += 1
+    el = time.perf_counter() - t0
+    out["paged_gqa_decode"] = {"GB/s": round(kv_bytes / el / 1e9, 4),
+                               "sample": f"sequences 0..{nb - 1} of {w.B} "
+                                         f"({el:.2f} s)"}
+    return out
+
+
+def machine_probe():
+    """Measured context for the roofline fractions: a pure bf16 MFMA loop on
+    every SIMD (attainable matrix-core rate, and the engine clock while it
+    runs) and a streaming read of 1 GiB (practical HBM read rate)."""
+    from exact_io_aware_15_amd import probe
+    tf, ghz, sec = probe.mfma_bf16(iters=40000, waves_per_simd=2)
+    gbs = probe.read_bw(1 << 30, 5)
+    return {"mfma_bf16_tflops": round(tf, 1), "clock_ghz_under_mfma":
+            round(ghz, 3), "mfma_loop_s": round(sec, 4),
+            "read_gbs": round(gbs, 1),
+            "note": "mfma: 4 independent v_mfma_f32_32x32x16_bf16 chains "
+                    "per wave, 2 waves per SIMD; read: grid-stride 16-byte "
+                    "non-temporal loads over 1 GiB"}
 
 
 def busy_counters(workload):
@@ -563,6 +717,7 @@ def main():
             r = sweep_one(args.sweep_only, args.steps, args.warmup, {})
         print(json.dumps({args.sweep_only: r}), flush=True)
         return
+    machine = None if args.no_probe else machine_probe()
     w = WORKLOADS[args.workload]
     attn = Attn(w)
     per_call = {}
@@ -616,7 +771,14 @@ def main():
                      "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_for(call)},
+                     "traffic": traffic_for(call),
+                     "measured_mfma_peak": None if machine is None else
+                     machine["mfma_bf16_tflops"],
+                     "frac_of_measured_mfma_peak": None if machine is None
+                     else round(achieved / machine["mfma_bf16_tflops"], 4),
+                     "clock_ghz_measured": None if machine is None else
+                     machine["clock_ghz_under_mfma"]},
+        "machine": machine,
         "kernel_source_hash": source_hash(),
         "io": {
             "unit": "bytes per call",
@@ -636,8 +798,15 @@ def main():
     del attn
     if not args.no_sweep:
         line["sweep"] = sweep(max(10, args.steps // 2), args.warmup)
+        dec = line["sweep"]["paged_gqa_decode"]["roofline"]
+        if machine is not None:
+            dec["measured_read_ceiling"] = machine["read_gbs"]
+            dec["frac_of_measured_read_ceiling"] = round(
+                dec["achieved"] / machine["read_gbs"], 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        line["cpu_baseline"]["configs"] = cpu_baseline_configs(
+            args.cpu_seconds * 1.5)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -5,8 +5,9 @@ Run as ``python -m exact_io_aware_15_amd.build``.  Each ``.hip`` source under
 objects are linked into ``exact_io_aware_15_amd/libfa355.so``.  The API source
 is compiled a second time with FA355_DEBUG defined and linked with the same
 kernel objects into ``libfa355_debug.so``, the build that checks the contents
-of the callers' device arrays.  hipcc cross-compiles gfx950 code without a GPU
-present.
+of the callers' device arrays.  The measurement kernels of probe/ (matrix-core
+rate, engine clock, streaming read rate) become ``libfa355_probe.so``.  hipcc
+cross-compiles gfx950 code without a GPU present.
 """
 
 import concurrent.futures as cf
@@ -23,6 +24,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa355.so")
 DEBUG_LIB = os.path.join(PKG, "libfa355_debug.so")
+PROBE_SRC = os.path.join(PKG, "probe", "fa_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libfa355_probe.so")
 
 ARCH = "gfx950"
 FLAGS = [
@@ -82,14 +85,15 @@ def build(verbose=False):
     the path of the ordinary library."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    jobs = [(s, False) for s in srcs] + [(API, True)]
+    jobs = [(s, False) for s in srcs] + [(API, True), (PROBE_SRC, False)]
     workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(workers) as ex:
         objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
-    api_obj, debug_obj = objs[srcs.index(API)], objs[-1]
+    api_obj, debug_obj, probe_obj = objs[srcs.index(API)], objs[-2], objs[-1]
     kernels = [o for o in objs[:len(srcs)] if o != api_obj]
     _link(kernels + [api_obj], LIB, verbose)
     _link(kernels + [debug_obj], DEBUG_LIB, verbose)
+    _link([probe_obj], PROBE_LIB, verbose)
     return LIB
 
 

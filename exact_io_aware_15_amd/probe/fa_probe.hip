@@ -1,0 +1,181 @@
+// fa_probe.hip -- measurement kernels for MI355X (gfx950): the attainable
+// bf16 matrix-core rate with the engine clock under that load, and a
+// streaming device-memory read.  Declared in include/fa355_probe.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa355_probe.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Four independent accumulation chains per wave, so consecutive MFMAs never
+// wait for each other's results; the operands are fixed non-zero values
+// (the rate does not depend on them).  Lane 0 of every wave records its core
+// cycles and constant-rate ticks; the accumulators are summed into `sink`
+// so the loop is not removed.
+__global__ __launch_bounds__(256) void mfma_loop_kernel(int iters,
+                                                        long long *cycles,
+                                                        long long *ticks,
+                                                        float *sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(1.0f + 0.001f * (lane + e));
+    b[e] = (__bf16)(0.5f - 0.001f * e);
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  const long long c0 = clock64(), w0 = wall_clock64();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+  }
+  const long long c1 = clock64(), w1 = wall_clock64();
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (lane == 0) {
+    cycles[wave] = c1 - c0;
+    ticks[wave] = w1 - w0;
+  }
+  if (s == 12345.678f) sink[0] = s;  // practically never taken
+}
+
+// Grid-stride read of n16 16-byte words, eight loads in flight per lane;
+// the words are XOR-folded into one value per thread so the loads stay.
+__global__ __launch_bounds__(256) void read_kernel(const u32x4 *src,
+                                                   size_t n16,
+                                                   uint32_t *sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t x = 0;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = src[i];
+    x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  if (x == 0x9e3779b9u) sink[0] = x;  // practically never taken
+}
+
+int fail(hipError_t e) { return e == hipSuccess ? FA_PROBE_OK : FA_PROBE_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_probe_mfma_bf16(int iters, int waves_per_simd, double *tflops,
+                       double *clock_ghz, double *seconds) {
+  if (iters < 1 || waves_per_simd < 1 || waves_per_simd > 4)
+    return FA_PROBE_E_ARG;
+  int dev = 0, cus = 0, wall_khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (!e) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (!e) e = hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev);
+  if (e) return fail(e);
+  // 256 threads = 4 waves, one per SIMD; waves_per_simd workgroups per CU.
+  const int blocks = cus * waves_per_simd;
+  const int waves = blocks * 4;
+  long long *cyc = nullptr, *tck = nullptr;
+  float *sink = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  e = hipMalloc(&cyc, sizeof(long long) * waves);
+  if (!e) e = hipMalloc(&tck, sizeof(long long) * waves);
+  if (!e) e = hipMalloc(&sink, sizeof(float));
+  if (!e) e = hipEventCreate(&e0);
+  if (!e) e = hipEventCreate(&e1);
+  float ms = 0.f;
+  if (!e) {
+    hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(256), 0, 0,
+                       iters / 10 + 1, cyc, tck, sink);  // warm-up
+    hipEventRecord(e0, 0);
+    hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(256), 0, 0, iters,
+                       cyc, tck, sink);
+    hipEventRecord(e1, 0);
+    e = hipEventSynchronize(e1);
+    if (!e) e = hipGetLastError();
+    if (!e) e = hipEventElapsedTime(&ms, e0, e1);
+  }
+  if (!e) {
+    long long *hc = new long long[waves], *ht = new long long[waves];
+    e = hipMemcpy(hc, cyc, sizeof(long long) * waves, hipMemcpyDeviceToHost);
+    if (!e) e = hipMemcpy(ht, tck, sizeof(long long) * waves, hipMemcpyDeviceToHost);
+    if (!e) {
+      double sc = 0, st = 0;
+      for (int w = 0; w < waves; ++w) {
+        sc += (double)hc[w];
+        st += (double)ht[w];
+      }
+      const double flop = (double)waves * iters * 4.0 * 32768.0;
+      if (tflops) *tflops = flop / (ms * 1e-3) / 1e12;
+      if (clock_ghz) *clock_ghz = st > 0 ? sc / st * wall_khz * 1e-6 : 0.0;
+      if (seconds) *seconds = ms * 1e-3;
+    }
+    delete[] hc;
+    delete[] ht;
+  }
+  if (e0) hipEventDestroy(e0);
+  if (e1) hipEventDestroy(e1);
+  hipFree(cyc);
+  hipFree(tck);
+  hipFree(sink);
+  return fail(e);
+}
+
+int fa_probe_read_bw(size_t bytes, int reps, double *gbs) {
+  if (bytes < (1u << 20) || bytes % (1u << 20) != 0 || reps < 1)
+    return FA_PROBE_E_ARG;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (!e) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e) return fail(e);
+  void *buf = nullptr;
+  uint32_t *sink = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  e = hipMalloc(&buf, bytes);
+  if (!e) e = hipMemset(buf, 1, bytes);
+  if (!e) e = hipMalloc(&sink, sizeof(uint32_t));
+  if (!e) e = hipEventCreate(&e0);
+  if (!e) e = hipEventCreate(&e1);
+  float ms = 0.f;
+  if (!e) {
+    const size_t n16 = bytes / 16;
+    const dim3 grid(cus * 8), block(256);
+    hipLaunchKernelGGL(read_kernel, grid, block, 0, 0, (const u32x4 *)buf,
+                       n16, sink);
+    hipEventRecord(e0, 0);
+    for (int r = 0; r < reps; ++r)
+      hipLaunchKernelGGL(read_kernel, grid, block, 0, 0, (const u32x4 *)buf,
+                         n16, sink);
+    hipEventRecord(e1, 0);
+    e = hipEventSynchronize(e1);
+    if (!e) e = hipGetLastError();
+    if (!e) e = hipEventElapsedTime(&ms, e0, e1);
+  }
+  if (!e && gbs) *gbs = (double)bytes * reps / (ms * 1e-3) / 1e9;
+  if (e0) hipEventDestroy(e0);
+  if (e1) hipEventDestroy(e1);
+  hipFree(buf);
+  hipFree(sink);
+  return fail(e);
+}
+
+}  // extern "C"

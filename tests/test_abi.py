@@ -262,3 +262,24 @@ def test_fp8_validation(lib):
     assert call(vt=ctypes.c_void_p(0x1008)) == -2   # not 16-byte aligned
     assert call(scale=-1.0) == -2
     assert call(d=96) == -3
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "fa355_probe.h")
+
+
+def test_probe_library_exports_and_validates():
+    """The measurement library exports what its header declares and rejects
+    invalid arguments before touching a device."""
+    from exact_io_aware_15_amd import probe
+    if not os.path.exists(probe.PROBE_LIB_PATH):
+        pytest.skip("libfa355_probe.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(fa_probe_[a-z0-9_]+)\s*\(", text)))
+    assert set(names) == set(probe.SIGNATURES)
+    h = probe.lib()
+    d = ctypes.c_double()
+    assert h.fa_probe_mfma_bf16(0, 2, None, None, None) == -1
+    assert h.fa_probe_mfma_bf16(10, 0, None, None, None) == -1
+    assert h.fa_probe_mfma_bf16(10, 5, None, None, None) == -1
+    assert h.fa_probe_read_bw(1000, 1, ctypes.byref(d)) == -1
+    assert h.fa_probe_read_bw(1 << 20, 0, ctypes.byref(d)) == -1
