@@ -737,7 +737,8 @@ def main():
     value = flops / step_ms / 1e9
     if bwd_ms >= fwd_ms:
         call, dur, cflops = "fa_bwd", bwd_ms, w.bwd_flops()
-        kern = "fa_bwd (bwd_pre + bwd_dkdv + bwd_dq launches)"
+        kern = ("fa_bwd (bwd_pre_kernel, then bwd_fused_kernel: the dK/dV "
+                "and dQ workgroups in one launch)")
     else:
         call, dur, cflops = "fa_fwd", fwd_ms, w.fwd_flops()
         kern = "fa_fwd (fwd_bf16_kernel)"

@@ -37,8 +37,10 @@ int fa_probe_mfma_bf16(int iters, int waves_per_simd, double *tflops,
 /*
  * fa_probe_read_bw -- streaming read rate of device memory: a buffer of
  * `bytes` (>= 1 MiB, a multiple of 1 MiB) is read `reps` (>= 1) times by a
- * grid-stride kernel of 16-byte loads (eight in flight per lane), timed with
- * HIP events after one untimed pass.  *gbs = bytes * reps / time / 1e9.
+ * grid-stride kernel of 16-byte non-temporal loads (eight in flight per
+ * lane), timed with HIP events after one untimed pass, at 1, 2, 4, 8 and 16
+ * workgroups of 256 threads per CU.  *gbs = bytes * reps / time / 1e9 of
+ * the fastest shape.
  */
 int fa_probe_read_bw(size_t bytes, int reps, double *gbs);
 
