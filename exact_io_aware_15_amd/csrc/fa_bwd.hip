@@ -407,6 +407,12 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs &a, int i) {
   }
   const float lrow = qi < N ? a.lse2[sr.row0 + qi] : INFINITY;
   const float drow = qi < N ? a.delta[sr.row0 + qi] : 0.f;
+  // -D of this lane's query in every register: the start value of each
+  // tile's dP^T accumulation, so the matrix cores return dP - D (not with
+  // dropout, where D stays outside the keep mask).
+  f32x16 negd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = DROP ? 0.f : -drow;
 
   f32x16 dq[D / 32];
 #pragma unroll
@@ -460,9 +466,9 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs &a, int i) {
       uint32_t ps[2][8];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        f32x16 s, dp;
+        f32x16 s, dp = negd;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
           const bf16x8 kf = lds_row_frag<D>(Kt, 32 * kb + ln, ks * 16 + 8 * hh);
@@ -499,7 +505,7 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs &a, int i) {
                                       : 0.f,
                                   -drow);
               else
-                dsv[u] = p * (dp[r] - drow);
+                dsv[u] = p * dp[r];  // dp already holds dP - D
             }
             ps[kb][i] = pack_bf16x2(dsv[0], dsv[1]);
           }
