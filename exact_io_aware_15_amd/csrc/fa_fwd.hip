@@ -34,12 +34,13 @@ constexpr float kRescaleLog2 = 8.0f;
 // Kt / Vt: S^T = K Q^T, the mask (diagonal and tail tiles only), the
 // running-max update, p = exp2(c*s - c*m_ref) rounded to bf16 once, l += sum p
 // and O^T += V^T P^T.  A tile wholly above the causal diagonal is skipped.
-template <int D, int QB, bool CAUSAL, bool DROP>
+template <int D, int QB, bool CAUSAL, bool DROP, bool LMF>
 __device__ __forceinline__ void fwd_tile(
     const uint16_t *Kt, const uint16_t *Vt, int k0, int qw, int kv_valid,
     int qoff, int bh, float c, const Dropout &drop,
     const bf16x8 (&qf)[QB][D / 16], f32x16 (&oacc)[QB][D / 32],
-    float (&m_ref)[QB], float (&m_max)[QB], float (&l_run)[QB]) {
+    float (&m_ref)[QB], float (&m_max)[QB], f32x4 (&l_acc)[QB],
+    const bf16x8 &lsel) {
   constexpr int QPW = 32 * QB;
   constexpr int BC = 64;
   const int lane = threadIdx.x & 63;
@@ -69,6 +70,7 @@ __device__ __forceinline__ void fwd_tile(
   // key k0 + 32*kb + 16*(r/8) + 8*hh + (r%8) of this lane's query.
   // pv[qb][kb][s2] is the B operand (8 consecutive keys) of P V.
   u32x4 pv[QB][2][2];
+  u32x4 pl[QB][2][2];  // the undropped p (the same as pv without dropout)
   float mcs[QB];
   u32x4 rnd[QB][2];
 #pragma unroll
@@ -116,7 +118,7 @@ __device__ __forceinline__ void fwd_tile(
       asm volatile("" ::: "memory");
       const float alpha = fast_exp2((m_ref[qb] - m_max[qb]) * c);
       m_ref[qb] = m_max[qb];
-      l_run[qb] *= alpha;
+      l_acc[qb] *= alpha;
 #pragma unroll
       for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
@@ -138,7 +140,7 @@ __device__ __forceinline__ void fwd_tile(
   // matrix cores work on them while the VALU computes block 1.  The V^T
   // fragment is read once (transposing LDS load) and used for every query
   // block; a query block whose keys are all masked contributes p = 0.
-  float lsum[QB];
+  float lsum[QB];  // row sums by dot products (when !LMF)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) lsum[qb] = 0.f;
 #pragma unroll
@@ -153,7 +155,7 @@ __device__ __forceinline__ void fwd_tile(
           const float p0 = fast_exp2(fmaf(s[qb][kb][r], c, -mcs[qb]));
           const float p1 = fast_exp2(fmaf(s[qb][kb][r + 1], c, -mcs[qb]));
           const uint32_t pu = pack_bf16x2(p0, p1);
-          lsum[qb] = dot2_ones(pu, lsum[qb]);
+          if (!LMF) lsum[qb] = dot2_ones(pu, lsum[qb]);
           if (DROP) {
             const uint32_t keep =
                 (drop_keep(rnd[qb][kb], r, drop.thr) ? 0xffffu : 0u) |
@@ -162,6 +164,7 @@ __device__ __forceinline__ void fwd_tile(
           } else {
             pv[qb][kb][s2][i] = pu;
           }
+          if (DROP && LMF) pl[qb][kb][s2][i] = pu;
         }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
@@ -173,9 +176,24 @@ __device__ __forceinline__ void fwd_tile(
           oacc[qb][cb] = mfma32(vf, __builtin_bit_cast(bf16x8, pv[qb][kb][s2]),
                                 oacc[qb][cb]);
       }
-  }
+    // Row sums on the matrix cores: l += (selector) x P for each 16-key
+    // group (the selector picks, per output row, the lanes of this lane's
+    // query).  Undropped p: l is the softmax normaliser.
+    if (LMF) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) l_run[qb] += lsum[qb];
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          l_acc[qb] = mfma16k32(
+              lsel, __builtin_bit_cast(bf16x8, DROP ? pl[qb][kb][s2]
+                                                    : pv[qb][kb][s2]),
+              l_acc[qb]);
+    }
+  }
+  if (!LMF) {  // per lane half; both halves are summed by the caller
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_acc[qb][0] += lsum[qb];
+  }
 }
 
 // Epilogue for one lane's query qi: O = o / l (0 for a row with no visible
@@ -223,6 +241,12 @@ template <int D, int QPW, bool CAUSAL, bool PADDED, bool PAGED = false,
           bool SPARSE = false, bool DROP = false, int MINW = 2>
 __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int QB = QPW / 32;                    // 32-query blocks per wave
+  // Row sums on the matrix cores (a 16x16x32 product per 16 keys, taking
+  // 16 VALU dot products off each tile) in the causal kernels, which keep
+  // their waves per SIMD with it.  The non-causal ones schedule a tile as
+  // one block and would need 4-50 more registers (losing a wave per SIMD or
+  // spilling), so they sum with dot products.
+  constexpr bool LMF = CAUSAL;
   constexpr int BR = 4 * QPW;                     // queries per workgroup
   constexpr int BC = 64;                          // keys per tile
   constexpr int CPR = D / 8;                      // 16-byte chunks per row
@@ -320,12 +344,26 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
     for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[qb][cb][r] = 0.f;
-  float m_ref[QB], m_max[QB], l_run[QB];
+  float m_ref[QB], m_max[QB];
+  // Row sum of this lane's query: in all four registers (LMF), or in
+  // register 0 over this lane's half of the keys (dot products).
+  f32x4 l_acc[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_ref[qb] = kMaxInit;  // raw (unscaled) score units
     m_max[qb] = kMaxInit;
-    l_run[qb] = 0.f;       // over this lane's half of the keys
+    l_acc[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // Selector A operand of the row-sum product (16 x 16 x 32): output row
+  // group j (rows 4j..4j+3) takes the contraction slots 8k..8k+7 with
+  // k % 2 == j % 2, i.e. the lanes that hold this lane's query, so lane l
+  // receives the row sum of query l % 32 (see fwd_tile).
+  bf16x8 lsel;
+  {
+    const __bf16 sel =
+        (__bf16)((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 1.0f : 0.0f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lsel[e] = sel;
   }
   const float c = a.c;
 
@@ -396,8 +434,9 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
     const uint16_t *Kt = Ks[buf];
     const uint16_t *Vt = Vs[buf];
 
-    fwd_tile<D, QB, CAUSAL, DROP>(Kt, Vt, k0, qw, kv_valid, qoff, bh, c,
-                                  a.drop, qf, oacc, m_ref, m_max, l_run);
+    fwd_tile<D, QB, CAUSAL, DROP, LMF>(Kt, Vt, k0, qw, kv_valid, qoff, bh, c,
+                                  a.drop, qf, oacc, m_ref, m_max, l_acc,
+                                  lsel);
 
     wait_dma();  // the next tile has landed
     __syncthreads();
@@ -414,8 +453,9 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
     fwd_store_rows<D, DROP>(a, hoff, sr.row0, qw + 32 * qb + ln, N,
-                            sum_xor32(l_run[qb]), m_ref[qb], m_max[qb],
-                            oacc[qb], 0, D / 32, hh == 0);
+                            LMF ? l_acc[qb][0] : sum_xor32(l_acc[qb][0]),
+                            m_ref[qb], m_max[qb], oacc[qb], 0, D / 32,
+                            hh == 0);
 }
 
 // fp32 path: one thread per query, 16-key tiles staged in LDS, the same
