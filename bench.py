@@ -579,13 +579,14 @@ def _visible_pairs(rows, n_keys, causal, kv):
 
 
 def cpu_baseline_configs(budget_s):
-    """The fp64 oracle on a bounded sample of every configuration: the
-    forward of each attention workload on one head's leading rows (rows
-    added until about budget_s / 8 seconds; causal rows see their prefix),
-    the backward of the three fwd+bwd workloads on one whole head, and the
-    paged decode on its first sequences.  Rates use the algorithmic counts
-    of the sample (4 d FLOP per visible pair forward, 10 d backward; K and
-    V bytes read for the decode)."""
+    """The fp64 oracle on a bounded sample of every configuration, each for
+    about budget_s / 8 seconds: the forward of each attention workload on
+    chunks of 256 rows of its heads in turn (causal rows see their prefix),
+    the backward of the three fwd+bwd workloads on whole heads in turn, and
+    the paged decode on its sequences in turn (a sample shorter than the
+    budget is repeated).  Rates use the algorithmic counts of the sample
+    (4 d FLOP per visible pair forward, 10 d backward; K and V bytes read
+    for the decode)."""
     import numpy as np
     import oracle
     from workloads import WORKLOADS
@@ -597,46 +598,63 @@ def cpu_baseline_configs(budget_s):
         w = WORKLOADS[name]
         q, k, v = w.qkv()
         kl = w.kv_len()
-        kv = w.N if kl is None else int(kl[0])
-        sl = (slice(0, 1), slice(0, 1))
-        klb = None if kl is None else kl[0:1]
-        t0, n, pairs = time.perf_counter(), 0, 0
+        heads = w.B * w.H
         step = min(w.N, 256)
-        while n < w.N:
-            rows = np.arange(n, min(w.N, n + step))
+        chunks = -(-w.N // step)
+        t0, it, pairs = time.perf_counter(), 0, 0
+        while True:   # chunk `it % chunks` of head `it // chunks % heads`
+            b, h = divmod(it // chunks % heads, w.H)
+            kv = w.N if kl is None else int(kl[b])
+            r0 = (it % chunks) * step
+            rows = np.arange(r0, min(w.N, r0 + step))
+            sl = (slice(b, b + 1), slice(h, h + 1))
             oracle.attention_fwd(q.exact[sl], k.exact[sl], v.exact[sl], None,
-                                 w.causal, klb, rows=rows)
+                                 w.causal, None if kl is None else kl[b:b + 1],
+                                 rows=rows)
             pairs += _visible_pairs(rows, w.N, w.causal, kv)
-            n += rows.size
+            it += 1
             if time.perf_counter() - t0 >= per:
                 break
         el = time.perf_counter() - t0
         e = {"fwd_tflops": round(4 * w.d * pairs / el / 1e12, 6),
-             "fwd_sample": f"head 0, rows 0..{n - 1} of {w.N} "
+             "fwd_sample": f"{it} chunks of up to {step} rows over "
+                           f"{min(heads, -(-it // chunks))} of {heads} heads "
                            f"({el:.2f} s)"}
         if w.backward:
             do = w.dout()
-            t0 = time.perf_counter()
-            oracle.attention_bwd(q.exact[sl], k.exact[sl], v.exact[sl],
-                                 do.exact[sl], None, w.causal, klb)
+            t0, nh, pairs = time.perf_counter(), 0, 0
+            while True:
+                b, h = divmod(nh % heads, w.H)
+                kv = w.N if kl is None else int(kl[b])
+                sl = (slice(b, b + 1), slice(h, h + 1))
+                oracle.attention_bwd(q.exact[sl], k.exact[sl], v.exact[sl],
+                                     do.exact[sl], None, w.causal,
+                                     None if kl is None else kl[b:b + 1])
+                pairs += _visible_pairs(np.arange(w.N), w.N, w.causal, kv)
+                nh += 1
+                if time.perf_counter() - t0 >= per:
+                    break
             el = time.perf_counter() - t0
-            allp = _visible_pairs(np.arange(w.N), w.N, w.causal, kv)
-            e["bwd_tflops"] = round(10 * w.d * allp / el / 1e12, 6)
-            e["bwd_sample"] = f"head 0, all {w.N} rows ({el:.2f} s)"
+            e["bwd_tflops"] = round(10 * w.d * pairs / el / 1e12, 6)
+            e["bwd_sample"] = f"{nh} whole heads ({el:.2f} s)"
         out[name] = e
     w = WORKLOADS["paged_gqa_decode"]
     q, cache = w.decode_inputs(poison_tails=False)
-    t0, nb = time.perf_counter(), 0
+    t0, it = time.perf_counter(), 0
     kv_bytes = 0
-    while nb < w.B and time.perf_counter() - t0 < per:
+    while True:
+        nb = it % w.B
         oracle.decode_paged(q.exact[nb:nb + 1], cache.k_cache.exact,
                             cache.v_cache.exact, cache.block_table[nb:nb + 1],
                             cache.seq_lens[nb:nb + 1])
         kv_bytes += int(cache.seq_lens[nb]) * w.Hkv * w.d * 2 * 2
-        nb += 1
+        it += 1
+        if time.perf_counter() - t0 >= per:
+            break
     el = time.perf_counter() - t0
     out["paged_gqa_decode"] = {"GB/s": round(kv_bytes / el / 1e9, 4),
-                               "sample": f"sequences 0..{nb - 1} of {w.B} "
+                               "sample": f"{it} sequence decodes over "
+                                         f"{min(it, w.B)} of {w.B} sequences "
                                          f"({el:.2f} s)"}
     return out
 
@@ -646,14 +664,15 @@ def machine_probe():
     every SIMD (attainable matrix-core rate, and the engine clock while it
     runs) and a streaming read of 1 GiB (practical HBM read rate)."""
     from exact_io_aware_15_amd import probe
-    tf, ghz, sec = probe.mfma_bf16(iters=40000, waves_per_simd=2)
+    tf, ghz, sec = probe.mfma_bf16(iters=120000, waves_per_simd=4)
     gbs = probe.read_bw(1 << 30, 5)
     return {"mfma_bf16_tflops": round(tf, 1), "clock_ghz_under_mfma":
             round(ghz, 3), "mfma_loop_s": round(sec, 4),
             "read_gbs": round(gbs, 1),
             "note": "mfma: 4 independent v_mfma_f32_32x32x16_bf16 chains "
-                    "per wave, 2 waves per SIMD; read: grid-stride 16-byte "
-                    "non-temporal loads over 1 GiB"}
+                    "per wave, 4 waves per SIMD, ~30 ms; read: grid-stride "
+                    "16-byte non-temporal loads over 1 GiB, best of 5 launch "
+                    "shapes"}
 
 
 def busy_counters(workload):
