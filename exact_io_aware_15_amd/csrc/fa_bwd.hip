@@ -98,8 +98,10 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs &a, int i) {
   // cores return dP - D (not with dropout, where D stays outside the mask).
   __shared__ __attribute__((aligned(16))) float LDs[2][2 * BR];
   __shared__ __attribute__((aligned(16))) float NDs[2][BR];
-  // lse2 by query (without dropout the interleaved pairs are not read: each
-  // lane fetches its 16 queries' lse2 and -D in eight 16-byte reads).
+  // -lse2 / c by query: the start value of the S accumulator (without
+  // dropout), so the matrix cores return S - lse2 / c and p = exp2(c s);
+  // each lane fetches its 16 queries' start values of S and dP in eight
+  // 16-byte reads, straight into the accumulators.
   __shared__ __attribute__((aligned(16))) float LSs[2][BR];
 
   const int tid = threadIdx.x;
@@ -161,6 +163,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs &a, int i) {
     for (int r = 0; r < 16; ++r) dk[cb][r] = dv[cb][r] = 0.f;
 
   const float c = a.c;
+  const float inv_c = 1.0f / c;
   const int q_begin = CAUSAL ? j0 : 0;
 
   // Double-buffered Q / dO blocks (DMA) and their row statistics; rows past
@@ -208,7 +211,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs &a, int i) {
       LDs[0][2 * tid] = l_nx;
       LDs[0][2 * tid + 1] = d_nx;
       NDs[0][tid] = -d_nx;
-      LSs[0][tid] = l_nx;
+      LSs[0][tid] = -l_nx * inv_c;
     }
   }
   wait_dma();
@@ -238,8 +241,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs &a, int i) {
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-      float lse_r[16];  // lse2 of register r's query (without dropout)
-      if (!DROP) {  // dp starts at -D of register r's query
+      if (!DROP) {  // s starts at -lse2/c, dp at -D of register r's query
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int qo = 32 * qb + 16 * (j >> 1) + 8 * hh + 4 * (j & 1);
@@ -248,7 +250,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs &a, int i) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             dp[4 * j + e] = nd[e];
-            lse_r[4 * j + e] = ls[e];
+            s[4 * j + e] = ls[e];
           }
         }
       }
@@ -282,8 +284,9 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs &a, int i) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const int r = 2 * i + t;
-            const float lse = DROP ? st[2 * t] : lse_r[r];
-            float p = fast_exp2(fmaf(s[r], c, -lse));
+            // without dropout s already holds S - lse2 / c
+            float p = DROP ? fast_exp2(fmaf(s[r], c, -st[2 * t]))
+                           : fast_exp2(s[r] * c);
             if (decltype(masked_tile)::value) {
               const bool masked =
                   key >= kv_valid || (CAUSAL && key > q0 + qo0 + t);
@@ -330,7 +333,7 @@ __device__ __forceinline__ void bwd_dkdv_body(const BwdArgs &a, int i) {
       LDs[buf ^ 1][2 * tid] = l_nx;
       LDs[buf ^ 1][2 * tid + 1] = d_nx;
       NDs[buf ^ 1][tid] = -d_nx;
-      LSs[buf ^ 1][tid] = l_nx;
+      LSs[buf ^ 1][tid] = -l_nx * inv_c;
     }
     wait_dma();
     __syncthreads();
