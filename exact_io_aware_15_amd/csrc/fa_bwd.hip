@@ -618,13 +618,13 @@ void bwd_launch_main(const BwdArgs &a, hipStream_t st) {
     const int n = nkt * a.BH;
     hipLaunchKernelGGL((bwd_fused_kernel<D, CAUSAL, PADDED, SPARSE, DROP>),
                        dim3((unsigned)(2 * n)), dim3(256), 0, st, a, n);
-    return;
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED, SPARSE, DROP>),
+                       dim3((unsigned)(nkt * a.BH)), dim3(256), 0, st, a);
+    const int nqt = (a.N + 127) / 128;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED, SPARSE, DROP>),
+                       dim3((unsigned)(nqt * a.BH)), dim3(256), 0, st, a);
   }
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, PADDED, SPARSE, DROP>),
-                     dim3((unsigned)(nkt * a.BH)), dim3(256), 0, st, a);
-  const int nqt = (a.N + 127) / 128;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, PADDED, SPARSE, DROP>),
-                     dim3((unsigned)(nqt * a.BH)), dim3(256), 0, st, a);
 }
 
 template <int D, bool CAUSAL>
