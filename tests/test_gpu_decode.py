@@ -91,3 +91,23 @@ def test_decode_invariant_to_block_placement():
     out2 = _run(q, cache, 4, table=table)
     assert np.array_equal(out1, out2)
     del torch
+
+
+@pytest.mark.parametrize("lens,splits", [
+    # more than 64 sequences: the split kernel keeps the batch's own order
+    ([17 + (37 * i) % 400 for i in range(70)], 4),
+    # tied lengths: the longest-first order breaks ties by sequence index
+    ([300, 300, 17, 300, 17, 1, 300, 0, 300], 3),
+])
+def test_decode_dispatch_order_cases(lens, splits):
+    B, Hq, Hkv, d = len(lens), 8, 2, 128
+    seed = 3200 + B
+    max_blocks = -(-max(lens) // 16) + 1
+    cache = paged_cache(lens, Hkv, d, 16, max_blocks, seed, poison_tails=True)
+    q = normal((B, Hq, d), seed, 0, "bf16")
+    print(f"decode order B={B} splits={splits}", flush=True)
+    out = _run(q, cache, splits)
+    assert_close("decode.out", out, _ref(q, cache), BF16_TOL)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(out[b] == 0)
