@@ -153,6 +153,8 @@ def source_hash():
     flags = [f for f in fa_build.FLAGS + fa_build.KERNEL_FLAGS
              if not os.path.isabs(f)]       # include paths vary by checkout
     h.update(" ".join(flags).encode())
+    for name in sorted(fa_build.SOURCE_FLAGS):
+        h.update((name + " " + " ".join(fa_build.SOURCE_FLAGS[name])).encode())
     return h.hexdigest()[:16]
 
 

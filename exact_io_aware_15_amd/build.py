@@ -49,6 +49,15 @@ def hipcc():
 # compiled without it.
 KERNEL_FLAGS = ["-fno-honor-nans"]
 
+# Extra flags for single sources, chosen by timing each kernel family with and
+# without them (outputs are bit-identical either way).  The backward kernels
+# gain 2-8% from the scheduler that favours instruction-level parallelism;
+# fa_bwd_nc128.hip holds the non-causal d = 128 backward kernels, which lose
+# under it and so keep the default.
+SOURCE_FLAGS = {
+    "fa_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
 
 API = os.path.join(CSRC, "fa_api.hip")
 
@@ -57,6 +66,7 @@ def _compile(src, verbose, debug=False):
     obj = os.path.join(BUILD, os.path.basename(src) +
                        (".debug.o" if debug else ".o"))
     extra = [] if src == API else KERNEL_FLAGS
+    extra = extra + SOURCE_FLAGS.get(os.path.basename(src), [])
     if debug:
         extra = extra + ["-DFA355_DEBUG"]
     cmd = [hipcc()] + FLAGS + extra + ["-c", src, "-o", obj]

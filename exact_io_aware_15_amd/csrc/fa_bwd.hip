@@ -20,6 +20,9 @@
 //             S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T.
 // At d = 64 (without dropout) passes 2 and 3 share one launch, their
 // workgroups interleaved (bwd_fused_kernel); otherwise they are two launches.
+// The non-causal d = 128 kernels are instantiated only in fa_bwd_nc128.hip
+// (this file built with FA355_BWD_NC128_UNIT defined), so that they can be
+// compiled with other scheduler options than the rest.
 // Recomputing S and dP in the dq pass costs two extra contractions; it
 // replaces the per-key-tile dQ partial sums that would otherwise need
 // device-wide float atomics, which are far slower on this part than the
@@ -648,11 +651,16 @@ hipError_t bwd_dispatch(const BwdArgs &a, hipStream_t st) {
 
 }  // namespace
 
+#ifdef FA355_BWD_NC128_UNIT
+hipError_t launch_bwd_nc128(const BwdArgs &a, hipStream_t s) {
+  return bwd_dispatch<128, false>(a, s);
+}
+#else
 hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, hipStream_t s) {
   if (d == 64)
     return causal ? bwd_dispatch<64, true>(a, s) : bwd_dispatch<64, false>(a, s);
-  return causal ? bwd_dispatch<128, true>(a, s)
-                : bwd_dispatch<128, false>(a, s);
+  return causal ? bwd_dispatch<128, true>(a, s) : launch_bwd_nc128(a, s);
 }
+#endif
 
 }  // namespace fa355

@@ -83,6 +83,8 @@ struct BwdArgs {
 };
 
 hipError_t launch_bwd(const BwdArgs &a, int d, bool causal, hipStream_t s);
+// The non-causal d = 128 case of launch_bwd, built in its own unit.
+hipError_t launch_bwd_nc128(const BwdArgs &a, hipStream_t s);
 
 struct DecodeArgs {
   const uint16_t *q;            // [B,Hq,d]
