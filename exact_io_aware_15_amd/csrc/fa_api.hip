@@ -4,6 +4,7 @@
 // call returns its status with no side effect (also on a machine with no GPU).
 #include <math.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "fa355.h"
@@ -137,9 +138,24 @@ int decode_validate(int B, int Hq, int Hkv, int d, const void *q,
   if (block_size != 16) return FA_E_UNSUPPORTED;
   if ((long long)B * max_blocks_per_seq > (1LL << 31) - 1 ||
       (long long)max_blocks_per_seq * 16 > (1LL << 31) - 1 ||
+      (long long)B * num_splits * Hq > (1LL << 31) - 1 ||
       (long long)num_blocks * block_size * Hkv * d > (1LL << 40))
     return FA_E_SHAPE;
   return FA_OK;
+}
+
+// Compute units of the current device, queried once per device.
+hipError_t compute_units(int *n) {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev >= 0 && dev < 64 && (*n = cached[dev].load()) > 0) return hipSuccess;
+  if (hipError_t e = hipDeviceGetAttribute(
+          n, hipDeviceAttributeMultiprocessorCount, dev))
+    return e;
+  if (*n < 1) *n = 1;
+  if (dev >= 0 && dev < 64) cached[dev].store(*n);
+  return hipSuccess;
 }
 
 // Enqueues a validated decode whose partial triples live at ws (laid out as
@@ -164,6 +180,7 @@ int decode_launch(int B, int Hq, int Hkv, int d, const void *q,
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.num_splits = num_splits;
+  if (hipError_t e = compute_units(&a.deal)) return from_hip(e);
   a.scale = scale;
   a.c = (float)((double)scale * 1.4426950408889634);
   hipStream_t s = (hipStream_t)stream;

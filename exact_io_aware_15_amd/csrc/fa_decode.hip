@@ -10,20 +10,24 @@
 // parallelism along queries, so the key range is split over workgroups and
 // their (m, l, o) triples are merged (FA notes §3.1 merge rule).
 //
-// Split kernel: grid (Hkv, num_splits, B), NW waves.  The G = Hq / Hkv query
-// heads of a group are MFMA columns 0 .. G-1 of a 16-column tile; GP >= G is
-// the group width the kernel is built for (a power of two, which sizes only
-// the LDS merge area), so every G <= 16 runs on the kernel of the next power
-// of two, the extra columns computing on zero queries and never stored.
-// Wave w of a split takes the split's blocks w, w + NW, ...; their table
-// entries sit one per lane.
-// Per block, on 16 x 16 matrix-core tiles (tokens x query heads of the
-// group): S^T = K Q^T with K read straight from HBM into registers, the
-// online-softmax update per head, then O^T += V^T P^T with V staged in LDS
-// by direct DMA and read back transposed.  While a block is computed, the
-// next block's K (registers) and V (the other LDS slot) are in flight.  The
+// Split kernel: one workgroup of NW waves per (sequence, split, KV head).
+// The G = Hq / Hkv query heads of a group are MFMA columns 0 .. G-1 of a
+// 16-column tile; GP >= G is the group width the kernel is built for (a
+// power of two, which sizes only the LDS merge area), so every G <= 16 runs
+// on the kernel of the next power of two, the extra columns computing on
+// zero queries and never stored.  Wave w of a split takes the split's blocks
+// w, w + NW, ...; their table entries sit one per lane.  The wave works on
+// them two at a time: it issues both blocks' K (straight from HBM into
+// registers) and V (into its two LDS slots by direct DMA), waits once, and
+// then, on 16 x 16 matrix-core tiles (tokens x query heads of the group),
+// computes S^T = K Q^T for both, one online-softmax update per head over
+// their 32 tokens, and O^T += V^T P^T with V read back transposed.  The
+// kernel is bound by the bytes in flight (each wave waits on its own loads
+// while the other waves' loads stream), so the pair doubles what a wave has
+// outstanding over one block at a time, without more registers or LDS.  The
 // NW per-wave states are merged through LDS into the split's triple.
-// Merge kernel: grid (Hq, B): out = sum_p w_p o_p / sum_p w_p l_p with
+// Merge kernel: one workgroup per (sequence, query head):
+// out = sum_p w_p o_p / sum_p w_p l_p with
 // w_p = exp2((m_p - max m) * scale * log2 e).
 #include "fa_device.h"
 #include "fa_kernels.h"
@@ -103,6 +107,19 @@ __device__ __forceinline__ int seq_by_length(const DecodeArgs &a, int z,
   return b;
 }
 
+// The work item of workgroup i.  The hardware deals consecutive workgroups
+// to different compute units, one per unit per round of `deal`, and every
+// workgroup of this launch is resident at once, so each unit's share is
+// fixed at dispatch; items come longest first, and odd rounds take them in
+// reverse, so that each unit's long and short items pair up (boustrophedon
+// order: for the 16-sequence decode the busiest unit's share drops from
+// 1.17 to 1.04 times the mean).  A permutation of 0 .. n-1.
+__device__ __forceinline__ int deal_order(int i, int n, int deal) {
+  const int r = i / deal, base = r * deal;
+  if (!(r & 1)) return i;
+  return base + min(deal, n - base) - 1 - (i - base);
+}
+
 // Four waves per SIMD (at most 128 registers per lane): with four-wave
 // workgroups a CU holds four of them, so a launch of up to 1024 workgroups
 // is resident at once and every wave keeps its next block's K and V in
@@ -126,12 +143,16 @@ __global__ __launch_bounds__(64 * NW, 4) void decode_split_kernel(
   };
   __shared__ __attribute__((aligned(16))) Smem sm;
 
-  // KV heads vary fastest: the Hkv workgroups of one (split, sequence) are
+  // One-dimensional grid of Hkv * S * B, walked through deal_order: KV heads
+  // vary fastest, so the Hkv workgroups of one (split, sequence) are
   // dispatched together and read neighbouring tiles of the same blocks;
-  // sequences go longest first.
-  const int hk = blockIdx.x, split = blockIdx.y;
+  // then splits; sequences go longest first.
+  const int item = deal_order(blockIdx.x, gridDim.x, a.deal);
+  const int hk = item % a.Hkv;
+  const int rest = item / a.Hkv;
+  const int split = rest % a.num_splits;
   int len;  // clamped to the table's capacity
-  const int b = seq_by_length(a, blockIdx.z, len);
+  const int b = seq_by_length(a, rest / a.num_splits, len);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;  // MFMA column / lane group
@@ -214,50 +235,73 @@ __global__ __launch_bounds__(64 * NW, 4) void decode_split_kernel(
                         reinterpret_cast<const u32x4 *>(kb + ks * 32)));
       dma_v_block<D>(slots[j & 1], a.v_cache + boff, tok_stride, n_valid);
     };
-    bf16x8 kc[KS], kn[KS];
-    fetch(0, kc);
-    for (int j = 0; j < n; ++j) {
-      wait_dma();  // block j's K and V have landed; nothing else in flight
-      if (j + 1 < n) fetch(j + 1, kn);
-      const int ph = __builtin_amdgcn_readlane(ent, j);
-      if (ph >= 0) {
-        const int t = tw0 + NW * (p0 + j);
-        const int n_valid = min(kBlock, len - t * kBlock);
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    // Valid tokens of block j (0 for a block that is absent, j >= n, or
+    // whose table entry is out of range: fetched from block 0 if at all,
+    // and never used).
+    auto valid_tokens = [&](int j) {
+      if (j >= n || __builtin_amdgcn_readlane(ent, j) < 0) return 0;
+      return min(kBlock, len - (tw0 + NW * (p0 + j)) * kBlock);
+    };
+    bf16x8 k0[KS], k1[KS];
+    for (int j = 0; j < n; j += 2) {
+      const bool two = j + 1 < n;
+      fetch(j, k0);
+      if (two) fetch(j + 1, k1);
+      wait_dma();  // both blocks' K and V have landed
+      const int nv0 = valid_tokens(j), nv1 = valid_tokens(j + 1);
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s = mfma16k32(kc[ks], qf[ks], s);
-        // Register r holds token 4*grp + r of head col.
-        float mx = -INFINITY;
+      for (int ks = 0; ks < KS; ++ks) s0 = mfma16k32(k0[ks], qf[ks], s0);
+      if (two) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s[r] = 4 * grp + r < n_valid ? s[r] : -INFINITY;
-          mx = fmaxf(mx, s[r]);
-        }
-        const float m_new = fmaxf(m_run, max_xor32(max_xor16(mx)));
-        const float alpha = fast_exp2((m_run - m_new) * c);
-        const float mc = m_new * c;
-        m_run = m_new;
-        u32x2 pb;
-        pb[0] = pack_bf16x2(fast_exp2(fmaf(s[0], c, -mc)),
-                            fast_exp2(fmaf(s[1], c, -mc)));
-        pb[1] = pack_bf16x2(fast_exp2(fmaf(s[2], c, -mc)),
-                            fast_exp2(fmaf(s[3], c, -mc)));
-        l_run = fmaf(l_run, alpha, dot2_ones(pb[1], dot2_ones(pb[0], 0.f)));
+        for (int ks = 0; ks < KS; ++ks) s1 = mfma16k32(k1[ks], qf[ks], s1);
+      }
+      // Register r holds token 4*grp + r of head col, in each block.
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s0[r] = 4 * grp + r < nv0 ? s0[r] : -INFINITY;
+        s1[r] = 4 * grp + r < nv1 ? s1[r] : -INFINITY;
+        mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+      }
+      const float m_new = fmaxf(m_run, max_xor32(max_xor16(mx)));
+      const float alpha = fast_exp2((m_run - m_new) * c);
+      const float mc = m_new * c;
+      m_run = m_new;
+      u32x2 pb0, pb1;
+      pb0[0] = pack_bf16x2(fast_exp2(fmaf(s0[0], c, -mc)),
+                           fast_exp2(fmaf(s0[1], c, -mc)));
+      pb0[1] = pack_bf16x2(fast_exp2(fmaf(s0[2], c, -mc)),
+                           fast_exp2(fmaf(s0[3], c, -mc)));
+      pb1[0] = pack_bf16x2(fast_exp2(fmaf(s1[0], c, -mc)),
+                           fast_exp2(fmaf(s1[1], c, -mc)));
+      pb1[1] = pack_bf16x2(fast_exp2(fmaf(s1[2], c, -mc)),
+                           fast_exp2(fmaf(s1[3], c, -mc)));
+      l_run = fmaf(l_run, alpha,
+                   dot2_ones(pb1[1], dot2_ones(pb1[0], dot2_ones(
+                       pb0[1], dot2_ones(pb0[0], 0.f)))));
+#pragma unroll
+      for (int cb = 0; cb < NC; ++cb) oacc[cb] = oacc[cb] * alpha;
+      // O^T += V^T P^T for each block that holds tokens (an absent block's
+      // slot is stale, a skipped one's may hold anything: neither is read
+      // into the arithmetic).
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if ((h ? nv1 : nv0) <= 0) continue;
+        const u32x2 pb = h ? pb1 : pb0;
         uint32_t vaj[NC];
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb)
-          vaj[cb] = va[cb] + (uint32_t)((j & 1) * TILE * 2);
+          vaj[cb] = va[cb] + (uint32_t)(h * TILE * 2);
         bf16x8 vf[NC / 2];  // two 16 x 16 V^T blocks per fragment
         lds_tr_frags(vf, vaj);
 #pragma unroll
         for (int cb = 0; cb < NC; ++cb) {
           const u32x4 w = __builtin_bit_cast(u32x4, vf[cb >> 1]);
           const u32x2 vb = (cb & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
-          oacc[cb] = mfma16k16(vb, pb, oacc[cb] * alpha);
+          oacc[cb] = mfma16k16(vb, pb, oacc[cb]);
         }
       }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kc[ks] = kn[ks];
     }
   }
   wait_dma();
@@ -308,7 +352,8 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
   // chunk's new max.  For up to eight partitions this is the plain merge:
   // m = max_p m_p, w_p = exp(m_p - m), out = sum w_p o_p / sum w_p l_p.
   constexpr int CH = 8;
-  const int hq = blockIdx.x, b = blockIdx.y, col = threadIdx.x;
+  const int hq = blockIdx.x % a.Hq, b = blockIdx.x / a.Hq;
+  const int col = threadIdx.x;
   const int S = a.num_splits;
   const size_t pbase = ((size_t)b * a.Hq + hq) * S;
   float mx = -INFINITY, acc = 0.f, lsum = 0.f;
@@ -347,9 +392,10 @@ hipError_t decode_dispatch_g(const DecodeArgs &a, hipStream_t s) {
   // per CU).
   constexpr int NW = 4;
   hipLaunchKernelGGL((decode_split_kernel<D, GP, NW>),
-                     dim3(a.Hkv, a.num_splits, a.B), dim3(64 * NW), 0, s, a);
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3(a.Hq, a.B), dim3(D), 0, s,
-                     a);
+                     dim3((unsigned)(a.Hkv * a.num_splits * a.B)),
+                     dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((unsigned)(a.Hq * a.B)),
+                     dim3(D), 0, s, a);
   return hipGetLastError();
 }
 

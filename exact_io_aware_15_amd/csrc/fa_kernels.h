@@ -96,6 +96,7 @@ struct DecodeArgs {
   float *part_m, *part_l;       // [B,Hq,S]
   float *part_o;                // [B,Hq,S,d]
   int B, Hq, Hkv, max_blocks, num_blocks, num_splits;
+  int deal;                     // compute units of the device
   float scale, c;
 };
 

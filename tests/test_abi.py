@@ -155,6 +155,12 @@ def test_decode_workspace_and_validation(lib):
     assert lib.fa_decode_paged(1, 32, 8, 128, FAKE, FAKE, FAKE, 100, 16, FAKE,
                                1 << 27, FAKE, 8, 0.1, FAKE, FAKE, ws,
                                NULL) == -2
+    # one workgroup per (partition slot, head): B * num_splits * Hq must fit
+    # an int
+    B = (1 << 31) // (64 * 32) + 1
+    assert lib.fa_decode_paged(B, 32, 8, 128, FAKE, FAKE, FAKE, 100, 16, FAKE,
+                               1, FAKE, 64, 0.1, FAKE, FAKE, 1 << 62,
+                               NULL) == -2
 
 
 def test_last_hip_error_starts_clear(lib):

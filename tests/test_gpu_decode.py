@@ -94,18 +94,28 @@ def test_decode_invariant_to_block_placement():
 
 
 @pytest.mark.parametrize("lens,splits", [
-    # more than 64 sequences: the split kernel keeps the batch's own order
+    # more than 64 sequences: every sequence is split into equal parts
     ([17 + (37 * i) % 400 for i in range(70)], 4),
-    # tied lengths: the longest-first order breaks ties by sequence index
+    # exactly 64 sequences: the largest batch that gets the split plan
+    ([1 + (53 * i) % 700 for i in range(64)], 3),
+    # tied lengths: slots go longest first, ties by sequence index
     ([300, 300, 17, 300, 17, 1, 300, 0, 300], 3),
+    # one split per sequence
+    ([5, 1000, 0, 160], 1),
+    # a single sequence over 63 partitions of a few blocks each
+    ([4000], 64),
+    # one long sequence among short ones: most partitions go to it
+    ([3000, 1, 2, 16, 17], 2),
+    # every sequence empty: no partition runs, every output is 0
+    ([0, 0, 0], 4),
 ])
-def test_decode_dispatch_order_cases(lens, splits):
+def test_decode_split_plan_cases(lens, splits):
     B, Hq, Hkv, d = len(lens), 8, 2, 128
     seed = 3200 + B
     max_blocks = -(-max(lens) // 16) + 1
     cache = paged_cache(lens, Hkv, d, 16, max_blocks, seed, poison_tails=True)
     q = normal((B, Hq, d), seed, 0, "bf16")
-    print(f"decode order B={B} splits={splits}", flush=True)
+    print(f"decode split plan B={B} splits={splits}", flush=True)
     out = _run(q, cache, splits)
     assert_close("decode.out", out, _ref(q, cache), BF16_TOL)
     for b, L in enumerate(lens):
