@@ -56,7 +56,8 @@ def test_prefill_small(ctx, qlen, Hq, Hkv, d, causal):
                                       cache.seq_lens, cu, None, causal)
     assert_close("prefill.o", o, ro, BF16_TOL)
     assert np.max(np.abs(m - rm) / np.maximum(1, np.abs(rm))) <= 1e-5
-    assert np.max(np.abs(l / rl - 1)) <= 2.0 ** -9 + 1e-5
+    # l sums bf16-rounded p: at most 2^-8 relative error per term
+    assert np.max(np.abs(l / rl - 1)) <= 2.0 ** -8 + 1e-5
 
 
 def test_prefill_workload_sampled_rows():
