@@ -291,9 +291,13 @@ def warm(fn, warmup):
 
 
 def time_step(attn, steps, warmup, backward=True, per_call=None):
-    """Run warmup steps, then `steps` timed steps with events around each
-    forward and backward call; returns mean ms of step, fwd and bwd (and,
-    if per_call is a dict, fills it with each call's percentiles)."""
+    """Run warmup steps, then `steps` timed steps bracketed by one event
+    and a synchronisation on each side (the step time), then `steps` more
+    with events around each forward and backward call (the split between
+    the two and each call's percentiles, filled into per_call if it is a
+    dict; those events cost a few microseconds per step, so they stay out
+    of the step time).  Returns mean ms of step, fwd and bwd, and the host
+    wall time per step of the first loop."""
     torch = attn.torch
 
     def one(_):
@@ -301,9 +305,18 @@ def time_step(attn, steps, warmup, backward=True, per_call=None):
         if backward:
             attn.bwd(o, m, l)
     warm(one, warmup)
+    s0, s1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s0.record()
+    for _ in range(steps):
+        one(None)
+    s1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    step_ms = s0.elapsed_time(s1) / steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
           for _ in range(steps)]
-    t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record()
         o, m, l = attn.fwd()
@@ -312,11 +325,9 @@ def time_step(attn, steps, warmup, backward=True, per_call=None):
             attn.bwd(o, m, l)
         ev[i][2].record()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps if backward \
         else 0.0
-    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / steps
     if per_call is not None:
         per_call["fwd"] = percentiles([e[0].elapsed_time(e[1]) for e in ev])
         if backward:
