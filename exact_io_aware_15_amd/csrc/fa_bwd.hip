@@ -42,8 +42,9 @@ namespace fa355 {
 namespace {
 
 // Rows are handled by groups of d/8 lanes (16 bytes of O and of dO each),
-// kPreRows rows per group with every load issued before any arithmetic, so
-// each lane keeps 2 * kPreRows loads in flight.  O is read only here, so its
+// kPreRows rows per group with every load (O, dO, and the row's m and l)
+// issued before any arithmetic, so each lane keeps 2 * kPreRows loads in
+// flight and a workgroup makes one round trip.  O is read only here, so its
 // loads are non-temporal; dO stays cached for the passes that follow.
 constexpr int kPreRows = 4;
 
@@ -56,14 +57,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   const long long r0 = ((long long)blockIdx.x * GPB + tid / CPR) * kPreRows;
   const int cc = tid % CPR;
   u32x4 o4[kPreRows], d4[kPreRows];
+  float mv[kPreRows], lv[kPreRows];
 #pragma unroll
   for (int k = 0; k < kPreRows; ++k) {
     const long long r = r0 + k;
     o4[k] = d4[k] = u32x4{0u, 0u, 0u, 0u};
+    mv[k] = lv[k] = 0.f;
     if (r < total) {
       o4[k] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4 *>(a.o + r * D + cc * 8));
       d4[k] = ldg128(a.dout + r * D + cc * 8);
+      if (cc == 0) {
+        mv[k] = a.m[r];
+        lv[k] = a.l[r];
+      }
     }
   }
 #pragma unroll
@@ -83,8 +90,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
       part += __shfl_xor(part, off, 64);
     if (cc == 0 && r < total) {
       a.delta[r] = part;
-      const float l = a.l[r];
-      a.lse2[r] = l > 0.f ? fmaf(a.m[r], kLog2e, __log2f(l)) : INFINITY;
+      a.lse2[r] = lv[k] > 0.f ? fmaf(mv[k], kLog2e, __log2f(lv[k])) : INFINITY;
     }
   }
 }
