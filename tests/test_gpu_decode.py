@@ -108,6 +108,9 @@ def test_decode_invariant_to_block_placement():
     ([3000, 1, 2, 16, 17], 2),
     # every sequence empty: no partition runs, every output is 0
     ([0, 0, 0], 4),
+    # 300 sequences x 64 splits x 2 KV heads: 38,400 workgroups in the
+    # one-dimensional grid, dealt over many rounds with a partial last one
+    ([1 + (7919 * i) % 100 for i in range(300)], 64),
 ])
 def test_decode_split_plan_cases(lens, splits):
     B, Hq, Hkv, d = len(lens), 8, 2, 128
