@@ -10,6 +10,7 @@ the library is missing, the calls raise.
     dq, dk, dv = bwd(q, k, v, o, do, m, l, causal=False, kv_len=None)
     o, m, l = fwd_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False)
     dq, dk, dv = bwd_varlen(q, k, v, o, do, m, l, cu_seqlens, max_seqlen)
+    k_cache = pack_k_cache(k_rows)      # [nb, Hkv, 16, d] -> K cache order
     out = decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits=8)
     o, m, l = prefill_paged(q, k_cache, v_cache, block_table, seq_lens,
                             cu_seqlens_q, max_q, causal=True)
@@ -24,7 +25,7 @@ from ._lib import FA_BF16, FA_F32, FaError, LibraryMissing, check, lib
 __all__ = ["fwd", "bwd", "fwd_dropout", "bwd_dropout", "fwd_fp8",
            "fwd_varlen", "bwd_varlen", "fwd_block_sparse",
            "bwd_block_sparse", "decode_paged", "decode_paged_noalloc",
-           "prefill_paged",
+           "prefill_paged", "pack_k_cache",
            "bwd_workspace_bytes", "bwd_varlen_workspace_bytes",
            "decode_workspace_bytes", "debug_flags", "CHECK_KV_LEN",
            "CHECK_CU_SEQLENS", "CHECK_SEQ_LENS", "CHECK_BLOCK_TABLE",
@@ -369,20 +370,45 @@ def bwd_varlen(q, k, v, o, do, m, l, cu_seqlens, max_seqlen, causal=False,
     return dq, dk, dv
 
 
+def _paged_cache_shape(k_cache, v_cache, d):
+    """Checks a paged cache pair against head dim d: v_cache [num_blocks,
+    Hkv, block_size, d], k_cache [num_blocks, Hkv, d/32, block_size, 32]
+    (grouped).  Returns (num_blocks, Hkv, block_size)."""
+    torch = _torch()
+    _check_dev("v_cache", v_cache, torch.bfloat16)
+    if v_cache.dim() != 4 or v_cache.shape[3] != d:
+        raise ValueError("v_cache must be [num_blocks, Hkv, block_size, d]")
+    nb, Hkv, bs, _ = v_cache.shape
+    _check_dev("k_cache", k_cache, torch.bfloat16,
+               (nb, Hkv, d // 32, bs, 32))
+    return nb, Hkv, bs
+
+
+def pack_k_cache(k_rows):
+    """A K cache held by token ([num_blocks, Hkv, block_size, d]) in the
+    library's grouped order [num_blocks, Hkv, d/32, block_size, 32]: entry
+    [.., g, u, j] is element 32g + j of token u.  A layout change for callers
+    that fill their cache by token; the paged calls read K in this order."""
+    nb, Hkv, bs, d = k_rows.shape
+    if d % 32:
+        raise ValueError("d must be divisible by 32")
+    return k_rows.reshape(nb, Hkv, bs, d // 32, 32).permute(
+        0, 1, 3, 2, 4).contiguous()
+
+
 def prefill_paged(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q,
                   max_q, causal=True, scale=None, return_stats=True):
     """New tokens of each sequence (packed [Hq, total_q, d] bf16) against a
-    paged cache [num_blocks, Hkv, 16, d] that already holds them; sequence
+    paged cache (v_cache [num_blocks, Hkv, 16, d], k_cache grouped
+    [num_blocks, Hkv, d/32, 16, 32], see pack_k_cache) that already holds
+    them;
+    sequence
     b's new tokens are its last cu[b+1]-cu[b] of seq_lens[b] positions.
     Returns (o, m, l) with m, l fp32 [Hq, total_q]."""
     torch = _torch()
     Hq, total_q, d = q.shape
-    nb, Hkv, bs, dk = k_cache.shape
     _check_dev("q", q, torch.bfloat16)
-    _check_dev("k_cache", k_cache, torch.bfloat16)
-    _check_dev("v_cache", v_cache, torch.bfloat16, k_cache.shape)
-    if dk != d:
-        raise ValueError("k_cache head dim differs from q")
+    nb, Hkv, bs = _paged_cache_shape(k_cache, v_cache, d)
     _check_dev("block_table", block_table, torch.int32)
     if block_table.dim() != 2:
         raise ValueError("block_table must be [B, max_blocks]")
@@ -416,18 +442,16 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits=8,
                  scale=None, workspace=None):
     """Single-token GQA decode over a paged cache.
 
-    q: [B,Hq,d] bf16; k_cache, v_cache: [num_blocks, Hkv, block_size, d] bf16;
+    q: [B,Hq,d] bf16; v_cache: [num_blocks, Hkv, block_size, d] bf16;
+    k_cache: [num_blocks, Hkv, d/32, block_size, 32] bf16 (grouped, see
+    pack_k_cache);
     block_table: int32 [B, max_blocks]; seq_lens: int32 [B].  Returns out
     [B,Hq,d] bf16.
     """
     torch = _torch()
     B, Hq, d = q.shape
-    nb, Hkv, bs, dk = k_cache.shape
     _check_dev("q", q, torch.bfloat16)
-    _check_dev("k_cache", k_cache, torch.bfloat16)
-    _check_dev("v_cache", v_cache, torch.bfloat16, k_cache.shape)
-    if dk != d:
-        raise ValueError("k_cache head dim differs from q")
+    nb, Hkv, bs = _paged_cache_shape(k_cache, v_cache, d)
     _check_dev("block_table", block_table, torch.int32)
     _check_dev("seq_lens", seq_lens, torch.int32, (B,))
     if block_table.dim() != 2 or block_table.shape[0] != B:
@@ -457,12 +481,8 @@ def decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens,
     call allocates nothing."""
     torch = _torch()
     B, Hq, d = q.shape
-    nb, Hkv, bs, dk = k_cache.shape
     _check_dev("q", q, torch.bfloat16)
-    _check_dev("k_cache", k_cache, torch.bfloat16)
-    _check_dev("v_cache", v_cache, torch.bfloat16, k_cache.shape)
-    if dk != d:
-        raise ValueError("k_cache head dim differs from q")
+    nb, Hkv, bs = _paged_cache_shape(k_cache, v_cache, d)
     _check_dev("block_table", block_table, torch.int32)
     _check_dev("seq_lens", seq_lens, torch.int32, (B,))
     if block_table.dim() != 2 or block_table.shape[0] != B:

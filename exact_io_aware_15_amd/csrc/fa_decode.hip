@@ -187,8 +187,10 @@ __global__ __launch_bounds__(64 * NW, 4) void decode_split_kernel(
   const float c = a.c;
 
   const int32_t *table = a.block_table + (size_t)b * a.max_blocks;
-  // Cache layout [num_blocks][Hkv][16][D]: one head's block tile is 16
-  // contiguous rows of D.
+  // Cache layouts: V [num_blocks][Hkv][16][D] (one head's block tile is 16
+  // contiguous rows of D); K [num_blocks][Hkv][D/32][16][32] (the same tile
+  // in 32-element groups: group g of the 16 tokens is 1 KiB contiguous).
+  // Both tiles of a head are 16*D elements at the same offset.
   constexpr size_t tok_stride = D;
   const size_t blk_stride = (size_t)Hkv * kBlock * D;
   const size_t head_off = (size_t)hk * kBlock * D;
@@ -220,19 +222,21 @@ __global__ __launch_bounds__(64 * NW, 4) void decode_split_kernel(
       ent = (ph >= 0 && ph < a.num_blocks) ? ph : -1;
     }
     // K of block j: lane (grp, col) loads token col (clamped to the valid
-    // ones), head dims 32*ks + 8*grp .. +7; V of block j goes to slot j % 2.
+    // ones), head dims 32*ks + 8*grp .. +7, i.e. part grp of the token's
+    // group ks, so each load instruction reads one contiguous 1 KiB group;
+    // V of block j goes to slot j % 2.
     auto fetch = [&](int j, bf16x8 (&kf)[KS]) {
       const int ph = __builtin_amdgcn_readlane(ent, j);
       const int t = tw0 + NW * (p0 + j);
       const int n_valid = min(kBlock, len - t * kBlock);  // >= 1
       const size_t boff = (size_t)max(ph, 0) * blk_stride + head_off;
-      const uint16_t *kb = a.k_cache + boff + (size_t)min(col, n_valid - 1) *
-                                                  tok_stride + 8 * grp;
+      const uint16_t *kb =
+          a.k_cache + boff + (size_t)min(col, n_valid - 1) * 32 + 8 * grp;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)  // read once: non-temporal
         kf[ks] = __builtin_bit_cast(
-            bf16x8, __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4 *>(kb + ks * 32)));
+            bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                        kb + ks * kBlock * 32)));
       dma_v_block<D>(slots[j & 1], a.v_cache + boff, tok_stride, n_valid);
     };
     // Valid tokens of block j (0 for a block that is absent, j >= n, or

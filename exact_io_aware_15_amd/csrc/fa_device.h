@@ -414,9 +414,11 @@ __device__ __attribute__((noinline)) void dma_tile_tail(uint16_t *tile,
 // The same fill for a 64-row key or value tile of a paged cache: logical
 // row t of the tile is token t % 16 of cache block blk[t / 16], whose 16 x W
 // tile for this KV head starts at base + blk * blk_stride (base already
-// points at the head's tile inside block 0).  Rows past last_row read row
-// last_row.  blk[] holds valid block indices.
-template <int W>
+// points at the head's tile inside block 0).  The block tile is row-major
+// (16 rows of W) or, with GROUPED, in 32-element groups (W/32 runs of 16
+// tokens x 32 elements: element 32 g + j of token u at (16 g + u) * 32 + j).
+// Rows past last_row read row last_row.  blk[] holds valid block indices.
+template <int W, bool GROUPED>
 __device__ __forceinline__ void dma_tile_paged(uint16_t *tile,
                                                const uint16_t *base,
                                                size_t blk_stride,
@@ -436,8 +438,11 @@ __device__ __forceinline__ void dma_tile_paged(uint16_t *tile,
     const int bi = t >> 4;
     const int b = bi == 0 ? blk[0] : bi == 1 ? blk[1] : bi == 2 ? blk[2]
                                                                  : blk[3];
-    const size_t goff = (size_t)b * blk_stride + (size_t)(t & 15) * W +
-                        (phys ^ lds_swz<W>(r)) * 8;
+    const int c = phys ^ lds_swz<W>(r);
+    const size_t goff =
+        (size_t)b * blk_stride +
+        (GROUPED ? (size_t)(16 * (c >> 2) + (t & 15)) * 32 + (c & 3) * 8
+                 : (size_t)(t & 15) * W + c * 8);
     __builtin_amdgcn_global_load_lds(
         (const __attribute__((address_space(1))) void *)(base + goff),
         (__attribute__((address_space(3))) void *)(tile + seg * 512), 16, 0,

@@ -386,8 +386,10 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
   const uint32_t slice_bytes = PAGED ? 0u : (uint32_t)N * D * 2;
   auto load_tile = [&](int k0, int buf) {
     if (PAGED) {
-      dma_tile_paged<D>(Ks[buf], kg, blk_stride, e_next, k0, kv_valid - 1);
-      dma_tile_paged<D>(Vs[buf], vg, blk_stride, e_next, k0, kv_valid - 1);
+      dma_tile_paged<D, true>(Ks[buf], kg, blk_stride, e_next, k0,
+                              kv_valid - 1);
+      dma_tile_paged<D, false>(Vs[buf], vg, blk_stride, e_next, k0,
+                               kv_valid - 1);
     } else if (k0 + BC <= kv_valid) {  // whole tile valid: uniform base
       dma_tile_at<D, BC>(Ks[buf], kg, slice_bytes, (uint32_t)k0 * D * 2,
                          doff);

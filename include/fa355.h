@@ -349,9 +349,10 @@ int fa_bwd_varlen(int B, int H, int total, int max_seqlen, int d,
  *                  fa_fwd_varlen).
  *   q, o           [Hq, total_q, d] bf16 (head-major packed); o written.
  *   m, l           [Hq, total_q] fp32 written, or both NULL.
- *   k_cache,
- *   v_cache        [num_blocks, Hkv, block_size, d] bf16, holding the K/V of
+ *   v_cache        [num_blocks, Hkv, block_size, d] bf16, holding the V of
  *                  every token of each sequence, its new tokens included.
+ *   k_cache        the same blocks of K, stored in 32-element groups as for
+ *                  fa_decode_paged: [num_blocks, Hkv, d/32, block_size, 32].
  *   block_size     16.
  *   max_blocks_per_seq  >= 1, with B * max_blocks_per_seq and
  *                  max_blocks_per_seq * 16 below 2^31 (else FA_E_SHAPE).
@@ -398,9 +399,14 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
  *                unused); above 16, FA_E_UNSUPPORTED.
  *   d            head dimension, 64 or 128.
  *   q            [B,Hq,d] bf16.
- *   k_cache,
  *   v_cache      [num_blocks, Hkv, block_size, d] bf16 (head-major within a
  *                block: one KV head's block_size x d tile is contiguous).
+ *   k_cache      [num_blocks, Hkv, d/32, block_size, 32] bf16: the same
+ *                tiles of K stored in 32-element groups, element 32g + j of
+ *                token u of a head's block at [.., g, u, j], so that group g
+ *                of the block's 16 tokens is 1 KiB contiguous (a layout of
+ *                this library; the pages index a block by token).  A head's
+ *                tile sits at the same offset in both caches.
  *                Slots past a sequence's length are never read into the
  *                arithmetic (they may hold anything, NaN included).
  *   block_size   tokens per block; 16.

@@ -44,6 +44,7 @@ from .reference import (  # noqa: F401
     attention_fwd,
     attention_bwd,
     decode_paged,
+    k_cache_rows,
     visible_mask,
 )
 from .online import (  # noqa: F401

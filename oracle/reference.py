@@ -24,7 +24,8 @@ import math
 
 import numpy as np
 
-__all__ = ["visible_mask", "attention_fwd", "attention_bwd", "decode_paged"]
+__all__ = ["visible_mask", "attention_fwd", "attention_bwd", "decode_paged",
+           "k_cache_rows"]
 
 
 def _default_scale(d, scale):
@@ -159,6 +160,24 @@ def attention_bwd(q, k, v, do, scale=None, causal=False, kv_len=None,
     return dq, dk, dv, D
 
 
+def k_cache_rows(k_cache):
+    """The paged K cache as token rows.
+
+    The library stores each KV head's block of K in groups of 32 head-dim
+    elements: entry [physical, head, g, u, j] is element 32*g + j of the
+    block's token u (shape [num_blocks, Hkv, d/32, block_size, 32]).  This is
+    a storage order of the library, not of the pages, which index a head's
+    block by token: the returned array is [num_blocks, Hkv, block_size, d]
+    with rows[physical, head, u, 32*g + j] = k_cache[physical, head, g, u, j].
+    The V cache is stored by token already.
+    """
+    k = np.asarray(k_cache)
+    nb, hkv, groups, bs, width = k.shape
+    if width != 32:
+        raise ValueError("K cache groups hold 32 elements")
+    return k.transpose(0, 1, 3, 2, 4).reshape(nb, hkv, bs, groups * 32)
+
+
 def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None):
     """Single-token GQA decode over a paged KV cache, by gather + softmax.
 
@@ -169,9 +188,10 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None):
     the group's shared KV head.  Reading: query head hq uses KV head
     hq // (Hq / Hkv) (consecutive query heads share a KV head).
 
-    q: [B,Hq,d]; k_cache, v_cache: [num_blocks, Hkv, block_size, d] (the
-    pages index one KV head's cache as cache[physical, :n]; with several
-    heads, each block keeps its heads one after another);
+    q: [B,Hq,d]; v_cache: [num_blocks, Hkv, block_size, d] (the pages index
+    one KV head's cache as cache[physical, :n]; with several heads, each
+    block keeps its heads one after another); k_cache: the same blocks of K
+    in the library's grouped order (``k_cache_rows``);
     block_table: int [B, max_blocks]; seq_lens: int [B].
     The plain definition is applied to the gathered keys: the method's loop is
     in ``online.paged_online``.  A sequence of length 0 gives out = 0.
@@ -179,6 +199,7 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale=None):
     """
     q = np.asarray(q, dtype=np.float64)
     B, Hq, d = q.shape
+    k_cache = k_cache_rows(k_cache)
     Hkv = k_cache.shape[1]
     bs = k_cache.shape[2]
     G = Hq // Hkv

@@ -23,6 +23,8 @@ import math
 
 import numpy as np
 
+from .reference import k_cache_rows
+
 __all__ = ["varlen_visible", "attention_fwd_varlen", "attention_bwd_varlen",
            "prefill_paged"]
 
@@ -125,12 +127,15 @@ def prefill_paged(q, k_cache, v_cache, block_table, seq_lens, cu_seqlens_q,
     new token i sits at position seq_lens[b] - qlen_b + i and, when causal,
     sees cached positions <= that one.
 
-    q: [Hq, total_q, d]; k_cache, v_cache: [num_blocks, Hkv, block_size, d];
+    q: [Hq, total_q, d]; v_cache: [num_blocks, Hkv, block_size, d]; k_cache:
+    the same blocks of K in the library's grouped order
+    (``reference.k_cache_rows``);
     block_table: [B, max_blocks]; seq_lens: [B].  Returns (o, m, l) with
     o [Hq, total_q, d] and m, l [Hq, total_q] as in the dense definition.
     """
     q = np.asarray(q, dtype=np.float64)
     Hq, total_q, d = q.shape
+    k_cache = k_cache_rows(k_cache)
     Hkv, bs = k_cache.shape[1], k_cache.shape[2]
     G = Hq // Hkv
     sc = _scale(d, scale)

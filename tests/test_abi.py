@@ -289,3 +289,24 @@ def test_probe_library_exports_and_validates():
     assert h.fa_probe_mfma_bf16(10, 5, None, None, None) == -1
     assert h.fa_probe_read_bw(1000, 1, ctypes.byref(d)) == -1
     assert h.fa_probe_read_bw(1 << 20, 0, ctypes.byref(d)) == -1
+
+
+def test_pack_k_cache_gives_the_generator_layout():
+    """pack_k_cache turns token-ordered K into the grouped cache order;
+    on the generator's own draw it must give the stored K bit for bit."""
+    import numpy as np
+    import torch
+
+    from exact_io_aware_15_amd import pack_k_cache
+    from workloads import TID_KC, bf16_bits, paged_cache, rng
+
+    cache = paged_cache([40, 9], 2, 64, 16, 3, cfg_seed=77, poison_tails=False)
+    nb = cache.v_cache.store.shape[0]
+    draw = rng(77, TID_KC).standard_normal(size=(nb, 2, 16, 64),
+                                           dtype=np.float32)
+    bits = torch.from_numpy(bf16_bits(draw).view(np.int16))
+    packed = pack_k_cache(bits)
+    assert packed.is_contiguous()
+    assert np.array_equal(packed.numpy().view(np.uint16), cache.k_cache.store)
+    with pytest.raises(ValueError):
+        pack_k_cache(torch.zeros(1, 1, 16, 48))

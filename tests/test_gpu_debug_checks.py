@@ -143,7 +143,7 @@ def _cache(lens, max_blocks, Hkv=2, d=64, seed=9503):
 
 
 def _decode(cache, table, seq_lens, Hq=4):
-    q = to_device(normal((len(seq_lens), Hq, cache.k_cache.exact.shape[-1]),
+    q = to_device(normal((len(seq_lens), Hq, cache.v_cache.exact.shape[-1]),
                          9504, 0, "bf16"))
     kc, vc = to_device(cache.k_cache), to_device(cache.v_cache)
     t, s = _i32(table), _i32(seq_lens)
@@ -180,7 +180,7 @@ def test_decode_bad_entries_and_lengths(builds):
 
 def _prefill(cache, table, seq_lens, cu, Hq=4):
     total = int(cu[-1])
-    d = cache.k_cache.exact.shape[-1]
+    d = cache.v_cache.exact.shape[-1]
     q = to_device(normal((Hq, total, d), 9505, 0, "bf16"))
     kc, vc = to_device(cache.k_cache), to_device(cache.v_cache)
     t, s, c = _i32(table), _i32(seq_lens), _i32(cu)

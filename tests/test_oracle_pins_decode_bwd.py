@@ -13,12 +13,62 @@ differences of L = sum(dO * O) and by identities the gradients must satisfy.
 import numpy as np
 import pytest
 
-from oracle import attention_bwd, attention_fwd, decode_paged, paged_online
-from workloads import paged_cache
+from oracle import (attention_bwd, attention_fwd, decode_paged, k_cache_rows,
+                    paged_online)
+from workloads import TID_KC, TID_VC, bf16_bits, paged_cache, rng as wl_rng
+
+
+def _grouped(kc):
+    """[nb, Hkv, bs, d] token rows -> the K cache order [nb, Hkv, d/32, bs,
+    32] (element 32g + j of token u at [.., g, u, j]), by explicit loops."""
+    nb, hkv, bs, d = kc.shape
+    out = np.empty((nb, hkv, d // 32, bs, 32), dtype=kc.dtype)
+    for g in range(d // 32):
+        for u in range(bs):
+            out[:, :, g, u, :] = kc[:, :, u, 32 * g:32 * g + 32]
+    return out
+
+
+def test_k_cache_rows_follows_the_documented_index():
+    """Entry [p, h, g, u, j] of the K cache is element 32g + j of token u of
+    head h in block p; k_cache_rows must put it at rows[p, h, u, 32g + j]."""
+    rng = np.random.default_rng(23)
+    k = rng.standard_normal((3, 2, 2, 5, 32))     # d = 64, block of 5
+    rows = k_cache_rows(k)
+    assert rows.shape == (3, 2, 5, 64)
+    for p in range(3):
+        for h in range(2):
+            for g in range(2):
+                for u in range(5):
+                    for j in range(32):
+                        assert rows[p, h, u, 32 * g + j] == k[p, h, g, u, j]
+    assert np.array_equal(k_cache_rows(_grouped(rows)), rows)
+    with pytest.raises(ValueError):
+        k_cache_rows(np.zeros((1, 1, 2, 4, 16)))
+
+
+def test_paged_cache_stores_k_grouped():
+    """The generator draws K and V as [nb, Hkv, bs, d] from their seeded
+    streams; V is stored as drawn, K at [.., g, u, j] = draw[.., u, 32g + j]."""
+    lens = np.array([20, 35])
+    cache = paged_cache(lens, 2, 64, 16, 3, cfg_seed=95, poison_tails=False)
+    nb = cache.v_cache.store.shape[0]
+    kd = wl_rng(95, TID_KC).standard_normal(size=(nb, 2, 16, 64),
+                                            dtype=np.float32)
+    vd = wl_rng(95, TID_VC).standard_normal(size=(nb, 2, 16, 64),
+                                            dtype=np.float32)
+    kbits, vbits = bf16_bits(kd), bf16_bits(vd)
+    assert cache.k_cache.store.shape == (nb, 2, 2, 16, 32)
+    assert np.array_equal(cache.v_cache.store, vbits)
+    for g in range(2):
+        for u in range(16):
+            assert np.array_equal(cache.k_cache.store[:, :, g, u, :],
+                                  kbits[:, :, u, 32 * g:32 * g + 32])
 
 
 def _contiguous_to_paged(Kc, Vc, block_size, rng):
-    """Scatter contiguous per-sequence K/V [L, Hkv, d] into a shuffled cache."""
+    """Scatter contiguous per-sequence K/V [L, Hkv, d] into a shuffled cache
+    (V by token, K in the grouped cache order)."""
     lens = [x.shape[0] for x in Kc]
     nblk = [-(-L // block_size) for L in lens]
     total = sum(nblk)
@@ -37,12 +87,12 @@ def _contiguous_to_paged(Kc, Vc, block_size, rng):
             kc[phys, :, :n] = Kc[b][rows].transpose(1, 0, 2)
             vc[phys, :, :n] = Vc[b][rows].transpose(1, 0, 2)
         off += nblk[b]
-    return kc, vc, table
+    return _grouped(kc), vc, table
 
 
 def test_paged_decode_equals_contiguous_attention():
     rng = np.random.default_rng(20)
-    B, Hq, Hkv, d, bs = 3, 8, 2, 16, 4
+    B, Hq, Hkv, d, bs = 3, 8, 2, 32, 4
     lens = [1, 13, 40]
     Kc = [rng.standard_normal((L, Hkv, d)) for L in lens]
     Vc = [rng.standard_normal((L, Hkv, d)) for L in lens]
@@ -63,8 +113,8 @@ def test_paged_decode_equals_contiguous_attention():
 def test_paged_decode_invariant_to_block_placement():
     rng = np.random.default_rng(21)
     lens = np.array([37, 64, 5])
-    cache = paged_cache(lens, 2, 8, 16, 4, cfg_seed=99)
-    q = rng.standard_normal((3, 4, 8))
+    cache = paged_cache(lens, 2, 32, 16, 4, cfg_seed=99)
+    q = rng.standard_normal((3, 4, 32))
     out = decode_paged(q, cache.k_cache.exact, cache.v_cache.exact,
                        cache.block_table, lens)
     # move every physical block to a new slot and rewrite the table to match
@@ -86,20 +136,20 @@ def test_paged_online_loop_equals_paged_definition():
     in ``decode_paged``)."""
     rng = np.random.default_rng(22)
     lens = np.array([1, 16, 17, 100])
-    cache = paged_cache(lens, 1, 8, 16, 7, cfg_seed=98)
-    q = rng.standard_normal((4, 1, 8))
+    cache = paged_cache(lens, 1, 32, 16, 7, cfg_seed=98)
+    q = rng.standard_normal((4, 1, 32))
     ref = decode_paged(q, cache.k_cache.exact, cache.v_cache.exact,
                        cache.block_table, lens)
     for b in range(4):
-        o = paged_online(q[b, 0], cache.k_cache.exact[:, 0],
+        o = paged_online(q[b, 0], k_cache_rows(cache.k_cache.exact)[:, 0],
                          cache.v_cache.exact[:, 0], cache.block_table[b],
                          int(lens[b]))
         assert np.max(np.abs(o - ref[b, 0])) <= 1e-13
 
 
 def test_paged_decode_empty_sequence_is_zero():
-    cache = paged_cache(np.array([0, 3]), 1, 4, 16, 2, cfg_seed=97)
-    out = decode_paged(np.ones((2, 2, 4)), cache.k_cache.exact,
+    cache = paged_cache(np.array([0, 3]), 1, 32, 16, 2, cfg_seed=97)
+    out = decode_paged(np.ones((2, 2, 32)), cache.k_cache.exact,
                        cache.v_cache.exact, cache.block_table, np.array([0, 3]))
     assert np.all(out[0] == 0) and np.all(np.isfinite(out[1]))
 

@@ -148,7 +148,8 @@ from workloads import paged_cache  # noqa: E402
 
 def _cache_from_packed(kp, vp, lens, bs, rng):
     """Scatter packed per-sequence K/V [Hkv, total, d] into a shuffled
-    head-major cache [num_blocks, Hkv, bs, d]; returns (kc, vc, table)."""
+    head-major cache (V [num_blocks, Hkv, bs, d], K in the grouped cache
+    order [num_blocks, Hkv, d/32, bs, 32]); returns (kc, vc, table)."""
     Hkv, _, d = kp.shape
     nblk = [-(-L // bs) for L in lens]
     total_blocks = max(1, sum(nblk))
@@ -166,14 +167,17 @@ def _cache_from_packed(kp, vp, lens, bs, rng):
             vc[phys, :, :n] = vp[:, tok + t * bs:tok + t * bs + n]
         off += nblk[b]
         tok += L
-    return kc, vc, table
+    grouped = np.empty((total_blocks, Hkv, d // 32, bs, 32))
+    for g in range(d // 32):
+        grouped[:, :, g] = kc[:, :, :, 32 * g:32 * g + 32]
+    return grouped, vc, table
 
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_prefill_from_empty_context_equals_varlen(causal):
     rng = np.random.default_rng([41, int(causal)])
     lens = [20, 1, 37, 16]
-    Hkv, G, d = 2, 2, 8
+    Hkv, G, d = 2, 2, 32
     cu = np.concatenate([[0], np.cumsum(lens)])
     kp = rng.standard_normal((Hkv, cu[-1], d))
     vp = rng.standard_normal((Hkv, cu[-1], d))
@@ -191,8 +195,8 @@ def test_prefill_from_empty_context_equals_varlen(causal):
 def test_prefill_of_one_token_equals_paged_decode():
     rng = np.random.default_rng(42)
     lens = np.array([1, 17, 40, 100])
-    cache = paged_cache(lens, 2, 8, 16, 8, cfg_seed=43)
-    q = rng.standard_normal((4, 8, 8))          # [B, Hq, d] one token each
+    cache = paged_cache(lens, 2, 32, 16, 8, cfg_seed=43)
+    q = rng.standard_normal((4, 8, 32))         # [B, Hq, d] one token each
     ref = decode_paged(q, cache.k_cache.exact, cache.v_cache.exact,
                        cache.block_table, lens)
     cu = np.arange(5)
@@ -204,7 +208,7 @@ def test_prefill_of_one_token_equals_paged_decode():
 
 def test_prefill_matches_brute_force_with_context():
     rng = np.random.default_rng(44)
-    L, qlen, d = 23, 6, 4
+    L, qlen, d = 23, 6, 32
     kp = rng.standard_normal((1, L, d))
     vp = rng.standard_normal((1, L, d))
     qfull = rng.standard_normal((L, d))
@@ -219,9 +223,9 @@ def test_prefill_matches_brute_force_with_context():
 def test_prefill_is_invariant_to_moving_blocks():
     rng = np.random.default_rng(45)
     lens = np.array([33, 70])
-    cache = paged_cache(lens, 1, 8, 16, 5, cfg_seed=46)
+    cache = paged_cache(lens, 1, 32, 16, 5, cfg_seed=46)
     cu = np.array([0, 9, 29])
-    q = rng.standard_normal((2, 29, 8))
+    q = rng.standard_normal((2, 29, 32))
     kc, vc = cache.k_cache.exact, cache.v_cache.exact
     o, _, _ = prefill_paged(q, kc, vc, cache.block_table, lens, cu)
     perm = rng.permutation(kc.shape[0])

@@ -31,7 +31,7 @@ def _call_both(lib, inp, splits):
     import torch
     q, kc, vc, table, lens = inp
     B, Hq, d = q.shape
-    nb, Hkv, bs, _ = kc.shape
+    nb, Hkv, bs, _ = vc.shape
     scale = 1.0 / d ** 0.5
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     need = lib.fa_decode_workspace_bytes(B, Hq, d, splits)

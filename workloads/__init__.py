@@ -140,7 +140,8 @@ def uniform_int(n, lo, hi, cfg_seed, tensor_id):
 
 @dataclass
 class Paged:
-    """A paged KV cache: [num_blocks, Hkv, block_size, d] plus block table."""
+    """A paged KV cache plus block table: V [num_blocks, Hkv, block_size, d],
+    K [num_blocks, Hkv, d/32, block_size, 32] (grouped, see paged_cache)."""
     k_cache: Tensor
     v_cache: Tensor
     block_table: np.ndarray   # int32 [B, max_blocks], -1 where unused
@@ -164,7 +165,16 @@ def paged_cache(seq_lens, Hkv, d, block_size, max_blocks, cfg_seed,
     """Random paged cache: every sequence's blocks are a slice of one random
     permutation of all physical blocks; slots past a sequence's length in its
     last block hold NaN when ``poison_tails`` (so a kernel that reads them
-    into its arithmetic is caught), else ordinary N(0,1) values."""
+    into its arithmetic is caught), else ordinary N(0,1) values.
+
+    V is stored [num_blocks, Hkv, block_size, d]; K in groups of 32 head-dim
+    elements, [num_blocks, Hkv, d/32, block_size, 32] (element 32g + j of
+    token u of a head's block at [.., g, u, j]), the library's K cache
+    layout.  Both draw their values as [num_blocks, Hkv, block_size, d]
+    arrays from their seeded streams, so the layout changes where a value
+    sits, not the value."""
+    if d % 32:
+        raise ValueError("paged caches need d divisible by 32")
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     B = seq_lens.size
     nblk = [-(-int(L) // block_size) for L in seq_lens]
@@ -185,6 +195,8 @@ def paged_cache(seq_lens, Hkv, d, block_size, max_blocks, cfg_seed,
                 last = table[b, nblk[b] - 1]
                 kc[last, :, L % block_size:] = np.nan
                 vc[last, :, L % block_size:] = np.nan
+    kc = np.ascontiguousarray(
+        kc.reshape(total, Hkv, block_size, d // 32, 32).transpose(0, 1, 3, 2, 4))
     kb, vb = bf16_bits(kc), bf16_bits(vc)
     return Paged(Tensor("bf16", kb, bf16_value(kb).astype(np.float64)),
                  Tensor("bf16", vb, bf16_value(vb).astype(np.float64)),
