@@ -450,6 +450,65 @@ __device__ __forceinline__ void dma_tile_paged(uint16_t *tile,
   }
 }
 
+// The same fill for a 64-row paged tile whose rows are all valid, with no
+// per-tile vector arithmetic.  One wave instruction fills 64 / (W / 8) storage
+// rows (4 at W = 128, 8 at W = 64) of one 16-row group, and row_perm moves
+// rows only inside such a group, so every instruction reads a single cache
+// block: its base is a scalar (blk_off[] holds the tile's four blocks as
+// wave-uniform element offsets, block index x block stride) and each lane's
+// byte offset inside the block's 16 x W tile is fixed.  The offsets are
+// computed once (PagedDmaOffsets); a tile then costs a scalar address and a
+// buffer resource per instruction.
+template <int W, bool GROUPED>
+struct PagedDmaOffsets {
+  static constexpr int SEGS = 64 * W * 2 / 1024;
+  static constexpr int ROWS_PER_SEG = 512 / W;
+  static_assert(16 % ROWS_PER_SEG == 0, "an instruction spans one block");
+  uint32_t off[SEGS / 4];
+  __device__ __forceinline__ PagedDmaOffsets() {
+    constexpr int CPR = W / 8;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int u = 0; u < SEGS / 4; ++u) {
+      const int p = (wave + 4 * u) * 64 + lane;
+      const int r = p / CPR, phys = p % CPR;
+      const int tok = ((r & ~31) | row_perm(r & 31)) & 15;
+      const int c = phys ^ lds_swz<W>(r);
+      off[u] = (uint32_t)(GROUPED ? ((16 * (c >> 2) + tok) * 32 + (c & 3) * 8) * 2
+                                  : (tok * W + c * 8) * 2);
+    }
+  }
+};
+
+template <int W, bool GROUPED>
+__device__ __forceinline__ void dma_tile_paged_at(
+    uint16_t *tile, const uint16_t *base, const size_t (&blk_off)[4],
+    const PagedDmaOffsets<W, GROUPED> &o) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // Segment wave + 4u of a 256-thread workgroup lies in block u (W = 128,
+  // 4 rows per segment) or 2u + wave / 2 (W = 64, 8 rows per segment).
+  // Constant indices keep blk_off[] in scalar registers.
+  constexpr int RPS = PagedDmaOffsets<W, GROUPED>::ROWS_PER_SEG;
+  static_assert(RPS == 4 || RPS == 8, "rows per segment");
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int u = 0; u < PagedDmaOffsets<W, GROUPED>::SEGS / 4; ++u) {
+    const int seg = wave + 4 * u;
+    size_t bo;
+    if (RPS == 4) {
+      bo = blk_off[u];
+    } else {
+      bo = wave >= 2 ? blk_off[2 * u + 1] : blk_off[2 * u];
+    }
+    const auto src = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(base + bo), (short)0, 16 * W * 2, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src, (__attribute__((address_space(3))) void *)(tile + seg * 512), 16,
+        o.off[u], 0, 0, 0);
+  }
+#endif
+}
+
 // Walks the allowed 128-wide blocks of one row (or column) of a block mask
 // in order.  The wave loads 64 mask bytes at once, one per lane, and keeps
 // them as a 64-bit ballot; next(t) is then a scalar bit scan except when a

@@ -372,20 +372,28 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
   // tile takes its four cache blocks from the table (entries loaded one
   // tile ahead of their use, clamped to valid block indices).
   const int nb_used = (kv_valid + 15) / 16;
+  size_t eo_next[4] = {0, 0, 0, 0};  // e_next as element offsets
   auto table_entries = [&](int t, int (&e)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = 4 * t + i;
-      e[i] = idx < nb_used ? min(max(btab[idx], 0), a.num_blocks - 1) : 0;
+      e[i] = __builtin_amdgcn_readfirstlane(
+          idx < nb_used ? min(max(btab[idx], 0), a.num_blocks - 1) : 0);
+      eo_next[i] = (size_t)e[i] * blk_stride;
     }
   };
   int e_next[4] = {0, 0, 0, 0};
   const DmaOffsets<D, BC> doff;
+  const PagedDmaOffsets<D, true> pk_off;
+  const PagedDmaOffsets<D, false> pv_off;
   // Whole tiles of a dense or packed slice go through buffer resources over
   // the slice's N rows (N <= 2^20, d <= 128: under 2^28 bytes).
   const uint32_t slice_bytes = PAGED ? 0u : (uint32_t)N * D * 2;
   auto load_tile = [&](int k0, int buf) {
-    if (PAGED) {
+    if (PAGED && k0 + BC <= kv_valid) {  // whole tile: uniform block bases
+      dma_tile_paged_at<D, true>(Ks[buf], kg, eo_next, pk_off);
+      dma_tile_paged_at<D, false>(Vs[buf], vg, eo_next, pv_off);
+    } else if (PAGED) {
       dma_tile_paged<D, true>(Ks[buf], kg, blk_stride, e_next, k0,
                               kv_valid - 1);
       dma_tile_paged<D, false>(Vs[buf], vg, blk_stride, e_next, k0,
