@@ -38,6 +38,9 @@ CASES = [  # (ctx lens, new-token counts, Hq, Hkv, d, causal)
     ([517, 40, 1000, 33], [200, 40, 7, 0], 8, 2, 64, False),
     ([700, 129], [300, 100], 8, 8, 128, True),
     ([700, 129], [300, 100], 4, 2, 128, False),
+    # contexts of whole 64-key tiles: the last tile is whole too
+    ([256, 640], [64, 640], 4, 2, 64, True),
+    ([640, 256], [100, 256], 8, 2, 128, False),
 ]
 
 
