@@ -69,6 +69,28 @@ def test_bwd_small(B, H, N, d, causal, padded):
     _check("small", q, k, v, do, causal, kv_len)
 
 
+# Few valid keys under many queries: each such key collects the dO of
+# hundreds of queries, so dK and dV reach magnitudes of 5-10, where bf16
+# rounding (of P, dS and the outputs) alone exceeds 2e-2 absolute; the
+# tolerance floor of one unit in the last place of the largest value
+# applies (see tests/helpers.py).  Shapes found by a randomized sweep.
+LARGE = [  # (B, H, N, d, causal, kv_len, seed)
+    (3, 1, 508, 64, False, [6, 379, 317], 550717758),
+    (3, 1, 99, 128, True, [2, 41, 80], 794539958),
+    (1, 1, 558, 64, True, [16], 764689141),
+    (3, 2, 188, 128, True, [62, 38, 5], 512586306),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,kv_len,seed", LARGE)
+def test_bwd_large_gradients(B, H, N, d, causal, kv_len, seed):
+    q, k, v = (normal((B, H, N, d), seed, t, "bf16") for t in range(3))
+    do = normal((B, H, N, d), seed, TID_DO, "bf16")
+    print(f"bwd large B={B} H={H} N={N} d={d} causal={causal} kv={kv_len}",
+          flush=True)
+    _check("large", q, k, v, do, causal, kv_len)
+
+
 def test_bwd_zero_length_sequence():
     q, k, v = (normal((2, 1, 96, 64), 81, t, "bf16") for t in range(3))
     do = normal((2, 1, 96, 64), 81, TID_DO, "bf16")

@@ -36,6 +36,9 @@ def _check(name, q, k, v, causal, kv_len, tol, rows=None, l_rel=None):
     assert_close(name + ".o", o, ro, tol)
     vis = np.isfinite(rm)
     assert np.array_equal(np.isfinite(m), vis), name + ".m finiteness"
+    if not vis.any():   # every key masked: nothing but zeros to check
+        assert np.all(l == 0) and np.all(o == 0)
+        return o
     assert np.max(np.abs(m[vis] - rm[vis]) / np.maximum(1, np.abs(rm[vis]))) \
         <= 1e-5, name + ".m"
     # l is summed from the bf16-rounded p that feeds the P V product.  bf16
@@ -96,6 +99,13 @@ def test_fwd_zero_length_rows_are_zero():
     assert np.all(o[0] == 0) and np.all(l[0] == 0) and np.all(np.isneginf(m[0]))
     ro, _, _ = oracle.attention_fwd(q.exact[1:], k.exact[1:], v.exact[1:])
     assert_close("kv0.o", o[1:], ro, BF16_TOL)
+
+
+def test_fwd_every_key_masked():
+    """kv_len = 0 for every sequence: all rows are empty (o = 0, l = 0)."""
+    q, k, v = (normal((2, 2, 130, 128), 79, t, "bf16") for t in range(3))
+    print("fwd kv_len all 0", flush=True)
+    _check("allmasked", q, k, v, True, [0, 0], BF16_TOL)
 
 
 def test_fwd_masked_keys_never_read_into_arithmetic():
