@@ -162,7 +162,7 @@ def attention_fwd_dropout(q, k, v, p_drop, seed, offset=0, scale=None,
 
 
 def attention_bwd_dropout(q, k, v, do, p_drop, seed, offset=0, scale=None,
-                          causal=False, kv_len=None, row_chunk=512):
+                          causal=False, kv_len=None, row_chunk=512, o=None):
     """Gradients of L = sum(dO * O) for O = attention_fwd_dropout(...).
 
     The chain rule with the mask Z held fixed (the pages print no backward
@@ -175,6 +175,12 @@ def attention_bwd_dropout(q, k, v, do, p_drop, seed, offset=0, scale=None,
         D_i = sum_j P_ij dP_ij           (equals sum_c dO_ic O_ic)
         dS = P * (dP - D)
         dQ = scale * dS K,   dK = scale * dS^T Q
+
+    o: None, or the stored forward output [B,H,N,d] that the backward reads
+    (FA notes §3.3 keeps O and (m, l) in HBM for the backward): then
+    D_i = sum_c dO_ic o_ic from it.  With the exact O this is the same D;
+    with O as stored in a narrower format it is the D such a backward forms,
+    and the gradients are those of the recomputation given that O.
 
     Returns (dq, dk, dv, D).
     """
@@ -200,7 +206,10 @@ def attention_bwd_dropout(q, k, v, do, p_drop, seed, offset=0, scale=None,
                 z = dropout_keep(b * H + h, rr, N, seed, offset, T) * ks
                 dv[b, h] += (p * z).T @ doi
                 dp = (doi @ v[b, h].T) * z
-                Di = (p * dp).sum(axis=1)
+                if o is None:
+                    Di = (p * dp).sum(axis=1)
+                else:
+                    Di = (doi * np.asarray(o[b, h, rr], np.float64)).sum(axis=1)
                 ds = p * (dp - Di[:, None])
                 dq[b, h, rr] = sc * (ds @ k[b, h])
                 dk[b, h] += sc * (ds.T @ qi)

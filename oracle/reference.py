@@ -108,7 +108,7 @@ def attention_fwd(q, k, v, scale=None, causal=False, kv_len=None, rows=None,
 
 
 def attention_bwd(q, k, v, do, scale=None, causal=False, kv_len=None,
-                  row_chunk=1024):
+                  row_chunk=1024, o=None):
     """Gradients of L = sum(dO * O) for O = attention_fwd(q, k, v), float64.
 
     The pages only say that the backward pass recomputes S and P from the
@@ -121,6 +121,12 @@ def attention_bwd(q, k, v, do, scale=None, causal=False, kv_len=None,
         dS = P * (dP - D)
         dQ = scale * dS K
         dK = scale * dS^T Q
+
+    o: None, or the stored forward output that the backward reads (FA notes
+    §3.3 keeps O and (m, l) in HBM for the backward): then D is the row sum of
+    dO * o.  With the exact O that is the same D; with O as stored in a
+    narrower format it is the D such a backward forms, and the gradients are
+    those of the recomputation given that O.
 
     Returns (dq, dk, dv, D) with D of shape [B,H,N].
     """
@@ -152,7 +158,10 @@ def attention_bwd(q, k, v, do, scale=None, causal=False, kv_len=None,
                 p, _, _ = _row_softmax(sc * (qi @ kj.T), vis)
                 dv[b, h, :kend] += p.T @ doi
                 dp = doi @ vj.T
-                Di = (p * dp).sum(axis=1)
+                if o is None:
+                    Di = (p * dp).sum(axis=1)
+                else:
+                    Di = (doi * np.asarray(o[b, h, rr], np.float64)).sum(axis=1)
                 ds = p * (dp - Di[:, None])
                 dq[b, h, rr] = sc * (ds @ kj)
                 dk[b, h, :kend] += sc * (ds.T @ qi)

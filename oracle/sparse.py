@@ -65,9 +65,17 @@ def attention_fwd_block_sparse(q, k, v, block_mask, block=128, scale=None,
 
 
 def attention_bwd_block_sparse(q, k, v, do, block_mask, block=128, scale=None,
-                               causal=False, row_chunk=512):
+                               causal=False, row_chunk=512, o=None):
     """Gradients of sum(dO * O) under the block mask (the chain rule of the
-    dense backward).  Returns (dq, dk, dv, D [B,H,N])."""
+    dense backward).
+
+    o: None, or the stored forward output that the backward reads (FA notes
+    §3.3 keeps O and (m, l) in HBM for the backward): then D is the row sum of
+    dO * o.  With the exact O that is the same D; with O as stored in a
+    narrower format it is the D such a backward forms, and the gradients are
+    those of the recomputation given that O.
+
+    Returns (dq, dk, dv, D [B,H,N])."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     B, H, N, d = q.shape
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -81,7 +89,11 @@ def attention_bwd_block_sparse(q, k, v, do, block_mask, block=128, scale=None,
                 p, _, _ = _softmax_rows(sc * (q[b, h, rr] @ k[b, h].T), vis)
                 dv[b, h] += p.T @ do[b, h, rr]
                 dp = do[b, h, rr] @ v[b, h].T
-                Di = (p * dp).sum(axis=1)
+                if o is None:
+                    Di = (p * dp).sum(axis=1)
+                else:
+                    Di = (do[b, h, rr] *
+                          np.asarray(o[b, h, rr], np.float64)).sum(axis=1)
                 ds = p * (dp - Di[:, None])
                 dq[b, h, rr] = sc * (ds @ k[b, h])
                 dk[b, h] += sc * (ds.T @ q[b, h, rr])

@@ -88,11 +88,19 @@ def attention_fwd_varlen(q, k, v, cu_seqlens, scale=None, causal=False,
 
 
 def attention_bwd_varlen(q, k, v, do, cu_seqlens, scale=None, causal=False,
-                         row_chunk=512):
+                         row_chunk=512, o=None):
     """Gradients of sum(dO * O) for O = attention_fwd_varlen(...), by the same
     chain rule as the dense backward (dV = P^T dO, dP = dO V^T,
     D = rowsum(P * dP), dS = P * (dP - D), dQ = scale dS K,
-    dK = scale dS^T Q).  Returns (dq, dk, dv, D [H, total])."""
+    dK = scale dS^T Q).
+
+    o: None, or the stored forward output that the backward reads (FA notes
+    §3.3 keeps O and (m, l) in HBM for the backward): then D is the row sum of
+    dO * o.  With the exact O that is the same D; with O as stored in a
+    narrower format it is the D such a backward forms, and the gradients are
+    those of the recomputation given that O.
+
+    Returns (dq, dk, dv, D [H, total])."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     H, total, d = q.shape
     sc = _scale(d, scale)
@@ -105,7 +113,10 @@ def attention_bwd_varlen(q, k, v, do, cu_seqlens, scale=None, causal=False,
             p, _, _ = _softmax_rows(sc * (q[h, rr] @ k[h].T), vis)
             dv[h] += p.T @ do[h, rr]
             dp = do[h, rr] @ v[h].T
-            Di = (p * dp).sum(axis=1)
+            if o is None:
+                Di = (p * dp).sum(axis=1)
+            else:
+                Di = (do[h, rr] * np.asarray(o[h, rr], np.float64)).sum(axis=1)
             ds = p * (dp - Di[:, None])
             dq[h, rr] = sc * (ds @ k[h])
             dk[h] += sc * (ds.T @ q[h, rr])

@@ -48,3 +48,18 @@ def assert_close(name, x, ref, tol):
         f"{name}: max-abs {err:.3e} (tol {abs_tol}), max-rel {rel:.3e} "
         f"(tol {rel_tol})")
     return err, rel
+
+
+def stored_forward(o, m, l):
+    """The oracle's forward outputs as a backward reads them from HBM: o
+    rounded to bf16 (returned as device bits and as the exact values of
+    those bits), m and l as fp32 device tensors."""
+    import torch
+    from workloads import bf16_bits, bf16_value
+    bits = bf16_bits(np.asarray(o, np.float32))
+    o_exact = bf16_value(bits).astype(np.float64)
+    o_dev = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+        torch.bfloat16).cuda()
+    m_dev = torch.from_numpy(np.asarray(m, np.float32)).cuda()
+    l_dev = torch.from_numpy(np.asarray(l, np.float32)).cuda()
+    return o_dev, o_exact, m_dev, l_dev

@@ -1,10 +1,20 @@
 """GPU parity on randomly drawn shapes (a fixed seed, so every run checks the
 same cases): dense forward + backward with causal masks and key padding,
-packed varlen forward + backward, paged GQA decode over group sizes 1-16 and
-1-64 splits, and paged prefill.  Lengths are drawn so that tails are ragged,
-sequences are empty or a single token, and some keys collect the dO of many
-queries.  Each case goes through the same checks and tolerances as the
-dedicated tests.
+packed varlen forward + backward, block-sparse and dropout forward +
+backward, paged GQA decode over group sizes 1-16 and 1-64 splits, and paged
+prefill.  Lengths are drawn so that tails are ragged, sequences are empty or
+a single token, and some keys collect the dO of many queries.  Each case goes
+through the same checks and tolerances as the dedicated tests.
+
+Every backward is also checked on its own: fed the oracle's forward outputs
+as they would sit in HBM (O rounded to bf16, m and l in fp32) and compared
+with the oracle's backward given that same stored O.  The row term
+D = rowsum(dO * O) is formed from the stored O, so against the exact
+gradient a backward carries O's rounding through D; when dS = P (dP - D)
+nearly cancels (one or two visible keys, or dropout's keep scale magnifying
+O) that term is all that is left of dQ and dK.  The end-to-end comparison
+(the GPU forward's outputs into the GPU backward, against the exact
+gradient) is kept for the dense and varlen kinds.
 """
 
 import numpy as np
@@ -16,13 +26,15 @@ from tests import test_gpu_decode as tdec
 from tests import test_gpu_fwd as tf
 from tests import test_gpu_prefill as tpre
 from tests import test_gpu_varlen as tv
-from tests.helpers import BF16_TOL, assert_close
+from tests import test_gpu_sparse as tsp
+from tests.helpers import BF16_TOL, assert_close, stored_forward, to_device
+from tests.helpers import to_numpy64
 from workloads import TID_DO, normal, paged_cache
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ("dense", "varlen", "decode", "prefill")
-PER_KIND = 12
+KINDS = ("dense", "varlen", "decode", "prefill", "sparse", "dropout")
+PER_KIND = 10
 
 
 def _draw(case):
@@ -51,6 +63,20 @@ def _draw(case):
                           G=int(rng.integers(1, 17)), d=d,
                           splits=int(rng.choice([1, 2, 3, 5, 8, 16, 64])),
                           spare=int(rng.integers(0, 3)), seed=seed)
+    if kind == "sparse":
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        return kind, dict(B=B, H=H, N=int(rng.integers(1, 900)), d=d,
+                          causal=causal, density=float(rng.uniform(0.1, 1)),
+                          seed=seed)
+    if kind == "dropout":
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        N = int(rng.integers(1, 600))
+        kv = ([int(x) for x in rng.integers(0, N + 1, size=B)]
+              if rng.integers(0, 2) else None)
+        return kind, dict(B=B, H=H, N=N, d=d, causal=causal, kv=kv,
+                          p=float(rng.choice([0.05, 0.1, 0.3, 0.5, 0.8])),
+                          dseed=int(rng.integers(0, 1 << 63)),
+                          off=int(rng.integers(0, 1 << 20)), seed=seed)
     ctx = [int(x) for x in rng.integers(1, 900, size=rng.integers(1, 5))]
     qlen = [int(rng.integers(0, c + 1)) for c in ctx]
     qlen[0] = max(qlen[0], 1)
@@ -59,18 +85,99 @@ def _draw(case):
                       seed=seed)
 
 
+def _grads(name, got, ref):
+    for g, r, n in zip(got, ref, ("dq", "dk", "dv")):
+        assert_close(f"{name}.{n}", to_numpy64(g), r, BF16_TOL)
+
+
+def _kv(kv):
+    import torch
+    return None if kv is None else torch.tensor(kv, dtype=torch.int32,
+                                                device="cuda")
+
+
 def _dense(B, H, N, d, causal, kv, seed):
+    import exact_io_aware_15_amd as fa
     q, k, v = (normal((B, H, N, d), seed, t, "bf16") for t in range(3))
     do = normal((B, H, N, d), seed, TID_DO, "bf16")
     tf._check("fwd", q, k, v, causal, kv, BF16_TOL)
     tb._check("bwd", q, k, v, do, causal, kv)
+    ro, rm, rl = oracle.attention_fwd(q.exact, k.exact, v.exact, None, causal,
+                                      kv)
+    o_dev, o_st, m_dev, l_dev = stored_forward(ro, rm, rl)
+    g = fa.bwd(to_device(q), to_device(k), to_device(v), o_dev, to_device(do),
+               m_dev, l_dev, causal=causal, kv_len=_kv(kv))
+    _grads("bwd-stored", g, oracle.attention_bwd(q.exact, k.exact, v.exact,
+                                                 do.exact, None, causal, kv,
+                                                 o=o_st))
 
 
 def _varlen(lens, H, d, causal, seed):
+    import torch
+    import exact_io_aware_15_amd as fa
     cu = tv._cu(lens)
     q, k, v = (normal((H, int(cu[-1]), d), seed, t, "bf16") for t in range(3))
+    do = normal((H, int(cu[-1]), d), seed, TID_DO, "bf16")
     tv._check_fwd("varlen", q, k, v, cu, causal, BF16_TOL)
     tv._bwd_case(lens, H, d, causal, seed)
+    ro, rm, rl = oracle.attention_fwd_varlen(q.exact, k.exact, v.exact, cu,
+                                             None, causal)
+    o_dev, o_st, m_dev, l_dev = stored_forward(ro, rm, rl)
+    g = fa.bwd_varlen(to_device(q), to_device(k), to_device(v), o_dev,
+                      to_device(do), m_dev, l_dev,
+                      torch.from_numpy(cu).cuda(), max(1, max(lens)),
+                      causal=causal)
+    _grads("varlen-stored", g, oracle.attention_bwd_varlen(
+        q.exact, k.exact, v.exact, do.exact, cu, None, causal, o=o_st))
+
+
+def _sparse(B, H, N, d, causal, density, seed):
+    import torch
+    import exact_io_aware_15_amd as fa
+    q, k, v = (normal((B, H, N, d), seed, t, "bf16") for t in range(3))
+    do = normal((B, H, N, d), seed, TID_DO, "bf16")
+    mask = tsp._mask(H, N, density, seed)
+    (o, m, l), _ = tsp._run(q, k, v, mask, causal)
+    ro, rm, rl = oracle.attention_fwd_block_sparse(q.exact, k.exact, v.exact,
+                                                   mask, 128, None, causal)
+    assert_close("sparse.o", o, ro, BF16_TOL)
+    vis = np.isfinite(rm)
+    assert np.array_equal(np.isfinite(m), vis)
+    if vis.any():
+        assert np.max(np.abs(m[vis] - rm[vis]) /
+                      np.maximum(1, np.abs(rm[vis]))) <= 1e-5
+        assert np.max(np.abs(l[vis] / rl[vis] - 1)) <= 2.0 ** -8 + 1e-5
+    o_dev, o_st, m_dev, l_dev = stored_forward(ro, rm, rl)
+    g = fa.bwd_block_sparse(to_device(q), to_device(k), to_device(v), o_dev,
+                            to_device(do), m_dev, l_dev,
+                            torch.from_numpy(mask).cuda(), causal=causal)
+    _grads("sparse-stored", g, oracle.attention_bwd_block_sparse(
+        q.exact, k.exact, v.exact, do.exact, mask, 128, None, causal,
+        o=o_st))
+
+
+def _dropout(B, H, N, d, causal, kv, p, dseed, off, seed):
+    import exact_io_aware_15_amd as fa
+    q, k, v = (normal((B, H, N, d), seed, t, "bf16") for t in range(3))
+    do = normal((B, H, N, d), seed, TID_DO, "bf16")
+    qd, kd, vd, dod = (to_device(x) for x in (q, k, v, do))
+    o, m, l = fa.fwd_dropout(qd, kd, vd, p, dseed, off, causal=causal,
+                             kv_len=_kv(kv))
+    o, m, l = (to_numpy64(x) for x in (o, m, l))
+    ro, rm, rl = oracle.attention_fwd_dropout(q.exact, k.exact, v.exact, p,
+                                              dseed, off, None, causal, kv)
+    assert_close("dropout.o", o, ro, BF16_TOL)
+    vis = np.isfinite(rm)
+    assert np.array_equal(np.isfinite(m), vis)
+    if vis.any():
+        assert np.max(np.abs(m[vis] - rm[vis]) /
+                      np.maximum(1, np.abs(rm[vis]))) <= 1e-5
+    o_dev, o_st, m_dev, l_dev = stored_forward(ro, rm, rl)
+    g = fa.bwd_dropout(qd, kd, vd, o_dev, dod, m_dev, l_dev, p, dseed, off,
+                       causal=causal, kv_len=_kv(kv))
+    _grads("dropout-stored", g, oracle.attention_bwd_dropout(
+        q.exact, k.exact, v.exact, do.exact, p, dseed, off, None, causal, kv,
+        o=o_st))
 
 
 def _decode(lens, Hkv, G, d, splits, spare, seed):
@@ -99,7 +206,7 @@ def _prefill(ctx, qlen, Hkv, G, d, causal, seed):
 
 
 RUN = {"dense": _dense, "varlen": _varlen, "decode": _decode,
-       "prefill": _prefill}
+       "prefill": _prefill, "sparse": _sparse, "dropout": _dropout}
 
 
 @pytest.mark.parametrize("case", range(PER_KIND * len(KINDS)))
