@@ -237,6 +237,22 @@ __device__ __forceinline__ void fwd_store_rows(const FwdArgs &a, size_t hoff,
 
 // MINW: waves per SIMD the register allocation must allow (4 caps a lane at
 // 128 VGPRs; 2 lets the compiler take what it needs).
+// Sequence with the z-th largest cached length (ties by index), for up to
+// 64 sequences; larger batches keep their own order.  Uniform in the wave.
+__device__ __forceinline__ int paged_seq_by_length(const FwdArgs &a, int z) {
+  if (a.B > 64) return z;
+  const int cap = a.max_blocks * 16;
+  const int lane = threadIdx.x & 63;
+  const int mine = lane < a.B ? min(max(a.seq_lens[lane], 0), cap) : -1;
+  int rank = 0;
+  for (int i = 0; i < a.B; ++i) {
+    const int li = __builtin_amdgcn_readlane(mine, i);
+    rank += (li > mine) || (li == mine && i < lane);
+  }
+  const uint64_t hit = __ballot(lane < a.B && rank == z);
+  return hit ? (int)__builtin_ctzll(hit) : 0;  // ranks are a permutation
+}
+
 template <int D, int QPW, bool CAUSAL, bool PADDED, bool PAGED = false,
           bool SPARSE = false, bool DROP = false, int MINW = 2>
 __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
@@ -263,8 +279,9 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
   // XCD's L2 when B*H is a multiple of 8 (or divides 8).  With a
   // paged cache the G query heads of one KV head read the same K/V tiles:
   // their workgroups get block indices of equal residue mod 8 (one XCD, one
-  // L2).  Unit u = (query-tile rank, sequence, KV head), G heads each; the
-  // grid is rounded up to whole groups of eight units.
+  // L2).  Unit u = (sequence rank, query tile, KV head), G heads each, the
+  // sequences ranked by cached length, longest first (a workgroup's work
+  // grows with it); the grid is rounded up to whole groups of eight units.
   const int nqt = (a.N + BR - 1) / BR;
   int bh, qt;
   if (PAGED) {
@@ -275,12 +292,14 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
     const int sx = bi >> 3;
     const int g = sx % G;
     const int u = (sx / G) * 8 + (bi & 7);
-    const int BHk = a.B * a.Hkv;
-    if (u >= nqt * BHk) return;  // rounding of the grid
-    const int bhk = u % BHk;
-    qt = nqt - 1 - u / BHk;
-    const int bb = bhk / a.Hkv;
-    bh = bb * a.H + (bhk - bb * a.Hkv) * G + g;
+    const int per_seq = nqt * a.Hkv;
+    if (u >= per_seq * a.B) return;  // rounding of the grid
+    // Sequences by decreasing cached length (a workgroup's work grows with
+    // it), then query tiles from the last, then KV heads.
+    const int rk = u / per_seq, rem = u - rk * per_seq;
+    qt = nqt - 1 - rem / a.Hkv;
+    const int bb = paged_seq_by_length(a, rk);
+    bh = bb * a.H + (rem % a.Hkv) * G + g;
   } else {
     // Resident workgroups per CU: 4 (MINW = 4), 3 (other d = 64), 2 (d = 128).
     const int i =

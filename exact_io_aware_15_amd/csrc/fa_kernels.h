@@ -26,9 +26,10 @@ struct FwdArgs {
   const int32_t *kv_len;   // [B] or null (dense only)
   const int32_t *cu_seqlens;  // [B+1] or null
   int total;               // packed rows per head (varlen)
-  // Paged prefill: keys and values come from a paged cache
-  // [num_blocks, Hkv, 16, d] through block_table [B, max_blocks]; sequence
-  // b's queries are the last positions of its seq_lens[b] cached tokens.
+  // Paged prefill: keys and values come from a paged cache (V
+  // [num_blocks, Hkv, 16, d], K [num_blocks, Hkv, d/32, 16, 32]) through
+  // block_table [B, max_blocks]; sequence b's queries are the last
+  // positions of its seq_lens[b] cached tokens.
   const void *k_cache, *v_cache;
   const int32_t *block_table, *seq_lens;
   int max_blocks, num_blocks, Hkv;
@@ -88,7 +89,7 @@ hipError_t launch_bwd_nc128(const BwdArgs &a, hipStream_t s);
 
 struct DecodeArgs {
   const uint16_t *q;            // [B,Hq,d]
-  const uint16_t *k_cache;      // [num_blocks, Hkv, block_size, d]
+  const uint16_t *k_cache;      // [num_blocks, Hkv, d/32, block_size, 32]
   const uint16_t *v_cache;
   const int32_t *block_table;   // [B, max_blocks]
   const int32_t *seq_lens;      // [B]
