@@ -41,6 +41,12 @@ CASES = [  # (ctx lens, new-token counts, Hq, Hkv, d, causal)
     # contexts of whole 64-key tiles: the last tile is whole too
     ([256, 640], [64, 640], 4, 2, 64, True),
     ([640, 256], [100, 256], 8, 2, 128, False),
+    # workgroups take sequences longest first: equal lengths (ties keep
+    # index order), and more than 64 sequences (taken in their own order)
+    ([300, 300, 300], [120, 7, 300], 4, 2, 128, True),
+    ([17 + (37 * i) % 200 for i in range(70)],
+     [1 + (11 * i) % (17 + (37 * i) % 200) for i in range(70)], 2, 1, 64,
+     True),
 ]
 
 
