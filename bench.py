@@ -218,7 +218,9 @@ class Attn:
             self.do = to_device(w.dout())
             kl = w.kv_len()
             self.kv_len = None if kl is None else torch.from_numpy(kl).cuda()
-            nbytes = fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d)
+            nbytes = (fa.bwd_block_sparse_workspace_bytes(w.B, w.H, w.N, w.d)
+                      if self.mask is not None else
+                      fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d))
         self.q, self.k, self.v = (to_device(t) for t in (q, k, v))
         self.ws = torch.empty(max(nbytes, 1), dtype=torch.uint8,
                               device="cuda")

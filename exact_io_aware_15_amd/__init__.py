@@ -27,6 +27,7 @@ __all__ = ["fwd", "bwd", "fwd_dropout", "bwd_dropout", "fwd_fp8",
            "bwd_block_sparse", "decode_paged", "decode_paged_noalloc",
            "prefill_paged", "pack_k_cache",
            "bwd_workspace_bytes", "bwd_varlen_workspace_bytes",
+           "bwd_block_sparse_workspace_bytes",
            "decode_workspace_bytes", "debug_flags", "CHECK_KV_LEN",
            "CHECK_CU_SEQLENS", "CHECK_SEQ_LENS", "CHECK_BLOCK_TABLE",
            "FaError", "LibraryMissing"]
@@ -160,6 +161,10 @@ def bwd_workspace_bytes(B, H, N, d):
     return int(lib().fa_bwd_workspace_bytes(B, H, N, d))
 
 
+def bwd_block_sparse_workspace_bytes(B, H, N, d):
+    return int(lib().fa_bwd_block_sparse_workspace_bytes(B, H, N, d))
+
+
 def bwd(q, k, v, o, do, m, l, causal=False, kv_len=None, scale=None,
         workspace=None):
     """Gradients (dq, dk, dv) of exact attention; all bf16 [B,H,N,d]."""
@@ -288,7 +293,7 @@ def bwd_block_sparse(q, k, v, o, do, m, l, block_mask, causal=False,
     block_mask = _block_mask(block_mask, H, N, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if workspace is None:
-        workspace = torch.empty(bwd_workspace_bytes(B, H, N, d),
+        workspace = torch.empty(bwd_block_sparse_workspace_bytes(B, H, N, d),
                                 dtype=torch.uint8, device=q.device)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     with torch.cuda.device(q.device):

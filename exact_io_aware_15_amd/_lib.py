@@ -35,6 +35,7 @@ SIGNATURES = {
     "fa_fwd_fp8": (_I, [_I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P,
                         _P, _P, _I, _F, _P]),
     "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I, _I]),
+    "fa_bwd_block_sparse_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _F,
                     _P, _P, _P, _P, _Z, _P]),
     "fa_fwd_dropout": (_I, [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _I,

@@ -304,6 +304,15 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   return 2 * align_up(rows * sizeof(float));
 }
 
+// The dense workspace, then the block-sparse items' work and order, each
+// [2][H * nb] int32.
+size_t fa_bwd_block_sparse_workspace_bytes(int B, int H, int N, int d) {
+  const size_t dense = fa_bwd_workspace_bytes(B, H, N, d);
+  if (!dense) return 0;
+  const size_t items = (size_t)H * ((N + 127) / 128);
+  return dense + 2 * align_up(2 * items * sizeof(int32_t));
+}
+
 int fa_bwd(int B, int H, int N, int d, const void *q, const void *k,
            const void *v, const void *o, const void *dout, const float *m,
            const float *l, const int32_t *kv_len, int causal, float scale,
@@ -369,10 +378,11 @@ int fa_bwd_block_sparse(int B, int H, int N, int d, const void *q,
     return FA_E_NULLPTR;
   if (!attn_shape_ok(B, H, N) || !valid_scale(scale)) return FA_E_SHAPE;
   if (d != 64 && d != 128) return FA_E_UNSUPPORTED;
-  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+  const size_t need = fa_bwd_block_sparse_workspace_bytes(B, H, N, d);
   if (!workspace || workspace_bytes < need) return FA_E_WORKSPACE;
   if (((uintptr_t)workspace) % kAlign) return FA_E_WORKSPACE;
   const size_t rows = (size_t)B * H * N;
+  const size_t items = (size_t)H * ((N + 127) / 128);
   BwdArgs a{};
   a.q = (const uint16_t *)q; a.k = (const uint16_t *)k;
   a.v = (const uint16_t *)v; a.o = (const uint16_t *)o;
@@ -382,6 +392,10 @@ int fa_bwd_block_sparse(int B, int H, int N, int d, const void *q,
   char *ws = (char *)workspace;
   a.lse2 = (float *)ws;
   a.delta = (float *)(ws + align_up(rows * sizeof(float)));
+  char *sp = ws + 2 * align_up(rows * sizeof(float));
+  a.sp_work = (int32_t *)sp;
+  a.sp_order = (int32_t *)(sp + align_up(2 * items * sizeof(int32_t)));
+  a.sp_causal = causal != 0;
   a.B = B; a.H = H; a.N = N; a.BH = B * H;
   a.scale = scale;
   a.c = (float)((double)scale * 1.4426950408889634);

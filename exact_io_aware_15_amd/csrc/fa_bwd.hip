@@ -48,6 +48,25 @@ namespace {
 // loads are non-temporal; dO stays cached for the passes that follow.
 constexpr int kPreRows = 4;
 
+// Block-sparse work of item t = (h, j): the dK/dV item of key block j of
+// head h visits the query blocks that mask column j allows (causal: i >= j),
+// the dQ item of query block j the key blocks that mask row j allows
+// (causal: i <= j).
+__device__ __forceinline__ void sparse_work(const BwdArgs &a, int t) {
+  const int nb = (a.N + 127) / 128;
+  const int n = a.H * nb;
+  if (t >= n) return;
+  const int h = t / nb, j = t - h * nb;
+  const uint8_t *m = a.block_mask + (size_t)h * nb * nb;
+  int col = 0, row = 0;
+  for (int i = 0; i < nb; ++i) {
+    col += (m[(size_t)i * nb + j] != 0) && (!a.sp_causal || i >= j);
+    row += (m[(size_t)j * nb + i] != 0) && (!a.sp_causal || i <= j);
+  }
+  a.sp_work[t] = col;
+  a.sp_work[n + t] = row;
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
   constexpr int CPR = D / 8;
@@ -93,6 +112,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
       a.lse2[r] = lv[k] > 0.f ? fmaf(mv[k], kLog2e, __log2f(lv[k])) : INFINITY;
     }
   }
+  // Block-sparse: one thread per (head, block) item counts its work (the
+  // grid has at least 2 H N threads, H * ceil(N / 128) are needed).
+  if (a.sp_work) sparse_work(a, blockIdx.x * 256 + tid);
 }
 
 template <int D, bool CAUSAL, bool PADDED, bool SPARSE, bool DROP>
@@ -569,13 +591,69 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs &a, int i) {
 
 // Causal: low key tiles carry most work; dealt so each CU's two resident
 // workgroups (d = 64) carry equal work.
+// The items of each pass in decreasing work, by a counting sort over the
+// work values 0 .. nb (nb <= 8192 for N <= 2^20): workgroup 0 orders the
+// dK/dV items, workgroup 1 the dQ items.  Items of equal work come in any
+// order (each item's result does not depend on when it runs).
+__global__ __launch_bounds__(1024) void sparse_order_kernel(BwdArgs a) {
+  constexpr int kMaxBins = 8193;
+  __shared__ int start[kMaxBins];
+  __shared__ int part[1024];
+  const int nb = (a.N + 127) / 128;
+  const int n = a.H * nb;
+  const int bins = nb + 1;
+  const int32_t *work = a.sp_work + (size_t)blockIdx.x * n;
+  int32_t *order = a.sp_order + (size_t)blockIdx.x * n;
+  const int tid = threadIdx.x;
+  for (int c = tid; c < bins; c += 1024) start[c] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) atomicAdd(&start[work[i]], 1);
+  __syncthreads();
+  // Bin c starts after every item of larger work.  Thread tid owns the
+  // bins at positions [tid * per, (tid + 1) * per) of the descending order.
+  const int per = (bins + 1023) / 1024;
+  const int r0 = min(bins, tid * per), r1 = min(bins, r0 + per);
+  int sum = 0;
+  for (int r = r0; r < r1; ++r) sum += start[bins - 1 - r];
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of part[]
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = tid ? part[tid - 1] : 0;
+  for (int r = r0; r < r1; ++r) {
+    const int c = bins - 1 - r;
+    const int cnt = start[c];
+    start[c] = run;
+    run += cnt;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) order[atomicAdd(&start[work[i]], 1)] = i;
+}
+
+// Block-sparse: the index, in the bodies' numbering, of pass `kind`'s item
+// at position idx of the heaviest-first order (positions r * B + b: the
+// r-th heaviest (head, block), batch b).
+__device__ __forceinline__ int sparse_item(const BwdArgs &a, int kind,
+                                           int idx) {
+  const int nb = (a.N + 127) / 128;
+  const int r = idx / a.B, b = idx - r * a.B;
+  const int it = a.sp_order[(size_t)kind * a.H * nb + r];
+  const int h = it / nb, blk = it - h * nb;
+  const int bh = b * a.H + h;
+  return kind == 0 ? blk * a.BH + bh : (nb - 1 - blk) * a.BH + bh;
+}
+
 template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false,
           bool DROP = false>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     BwdArgs a) {
-  const int i = (CAUSAL && !SPARSE)
-                    ? causal_deal_order<D == 64 ? 2 : 1>(blockIdx.x)
-                    : (int)blockIdx.x;
+  const int i = SPARSE ? sparse_item(a, 0, blockIdx.x)
+                : CAUSAL ? causal_deal_order<D == 64 ? 2 : 1>(blockIdx.x)
+                         : (int)blockIdx.x;
   bwd_dkdv_body<D, CAUSAL, PADDED, SPARSE, DROP>(a, i);
 }
 
@@ -585,16 +663,17 @@ template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false,
           bool DROP = false>
 __global__ __launch_bounds__(256, D == 64 ? 3 : 1) void bwd_dq_kernel(
     BwdArgs a) {
-  const int i = (CAUSAL && !SPARSE)
-                    ? causal_deal_order<D == 64 ? 3 : 1>(blockIdx.x)
-                    : (int)blockIdx.x;
+  const int i = SPARSE ? sparse_item(a, 1, blockIdx.x)
+                : CAUSAL ? causal_deal_order<D == 64 ? 3 : 1>(blockIdx.x)
+                         : (int)blockIdx.x;
   bwd_dq_body<D, CAUSAL, PADDED, SPARSE, DROP>(a, i);
 }
 
 // Both passes in one launch of 2n workgroups (n of each kind): the grid
 // alternates rounds of 256 workgroups between the two kinds, so a CU's two
 // resident workgroups are one of each (their instruction mixes differ) and
-// the tail of one pass overlaps the other.  Heaviest first within a kind.
+// the tail of one pass overlaps the other.  Heaviest first within a kind
+// (block-sparse: in the order of the items' work counts).
 template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false,
           bool DROP = false>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_fused_kernel(
@@ -611,6 +690,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_fused_kernel(
     kind = j >= rem;
     idx = 256 * full + (kind ? j - rem : j);
   }
+  if (SPARSE) idx = sparse_item(a, kind, idx);
   if (kind == 0)
     bwd_dkdv_body<D, CAUSAL, PADDED, SPARSE, DROP>(a, idx);
   else
@@ -642,8 +722,14 @@ hipError_t bwd_dispatch(const BwdArgs &a, hipStream_t st) {
   const long long rpb = 256 / (D / 8) * kPreRows;
   hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)),
                      dim3(256), 0, st, a);
-  if (a.block_mask)
+  if (a.block_mask) {
+    // Items heaviest first: the work of a (head, block) item, counted by
+    // bwd_pre_kernel above, is the number of blocks its mask column (dK/dV)
+    // or row (dQ) allows, and a column that every row allows can carry
+    // many times the average.
+    hipLaunchKernelGGL(sparse_order_kernel, dim3(2), dim3(1024), 0, st, a);
     bwd_launch_main<D, CAUSAL, false, true>(a, st);
+  }
   else if (a.drop.thr != 0 && a.kv_len)
     bwd_launch_main<D, CAUSAL, true, false, true>(a, st);
   else if (a.drop.thr != 0)

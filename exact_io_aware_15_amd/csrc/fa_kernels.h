@@ -79,6 +79,11 @@ struct BwdArgs {
   uint16_t *dq, *dk, *dv;                // [B,H,N,d] bf16
   float *lse2;                           // [B,H,N] workspace: log2-domain row offset
   float *delta;                          // [B,H,N] workspace: rowsum(dO*O)
+  // Block-sparse only (else null), workspace [2][H*nb] each, nb = N/128
+  // rounded up: the work of every (head, block) item of the two passes
+  // (dK/dV items, then dQ items), and the items of each pass heaviest first.
+  int32_t *sp_work, *sp_order;
+  int sp_causal;                         // the mask is causal (block-sparse)
   int B, H, N, BH;
   float scale, c;
 };

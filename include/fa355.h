@@ -263,10 +263,24 @@ int fa_fwd_block_sparse(int B, int H, int N, int d, const void *q,
                         float scale, void *stream);
 
 /*
+ * fa_bwd_block_sparse_workspace_bytes -- device workspace fa_bwd_block_sparse
+ * needs: fa_bwd_workspace_bytes(B, H, N, d) plus two [2][H * ceil(N/128)]
+ * int32 arrays (the work of each (head, 128-block) item of the two passes,
+ * and the items ordered heaviest first), each padded to 256 bytes.  Returns
+ * 0 for shapes fa_bwd_workspace_bytes rejects.
+ */
+size_t fa_bwd_block_sparse_workspace_bytes(int B, int H, int N, int d);
+
+/*
  * fa_bwd_block_sparse -- gradients of fa_fwd_block_sparse (the chain rule
  * of fa_bwd under the mask; masked blocks are skipped).  Arguments as for
- * fa_bwd without kv_len, plus the same block_mask; the workspace is
- * fa_bwd_workspace_bytes(B, H, N, d) bytes.  Keys no query sees get
+ * fa_bwd without kv_len, plus the same block_mask; the workspace (256-byte
+ * aligned, contents on entry ignored) is at least
+ * fa_bwd_block_sparse_workspace_bytes(B, H, N, d) bytes, else
+ * FA_E_WORKSPACE.  Two small kernels first count the blocks each key
+ * column and query row of the mask allows and sort the (head, block) items
+ * by that count, so the items with most work start first (a column every
+ * row allows can carry many times the average).  Keys no query sees get
  * dk = dv = 0; queries that see no key get dq = 0.
  */
 int fa_bwd_block_sparse(int B, int H, int N, int d, const void *q,

@@ -97,6 +97,13 @@ def test_bwd_workspace_and_validation(lib):
     assert ws == 2 * up(rows * 4)
     assert lib.fa_bwd_workspace_bytes(2, 3, 100, 80) == 0
     assert lib.fa_bwd_workspace_bytes(0, 3, 100, 64) == 0
+    # block-sparse: the dense workspace plus [2][H * ceil(N/128)] int32 work
+    # counts and orders, each padded to 256 bytes
+    sp = lib.fa_bwd_block_sparse_workspace_bytes(2, 3, 300, 64)
+    dense = lib.fa_bwd_workspace_bytes(2, 3, 300, 64)
+    assert sp == dense + 2 * 256                # 2 * 3 * 3 * 4 = 72 bytes
+    assert lib.fa_bwd_block_sparse_workspace_bytes(2, 3, 100, 80) == 0
+    assert lib.fa_bwd_block_sparse_workspace_bytes(0, 3, 100, 64) == 0
 
     def call(ws_ptr=FAKE, ws_bytes=ws, d=64, q=FAKE, N=100, scale=0.125):
         return lib.fa_bwd(2, 3, N, d, q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
@@ -228,6 +235,8 @@ def test_block_sparse_validation(lib):
     assert bwd(mask=NULL) == -1
     assert bwd(ws=NULL) == -4
     assert bwd(ws_bytes=16) == -4
+    # the dense backward's workspace lacks the items' work and order arrays
+    assert bwd(ws_bytes=lib.fa_bwd_workspace_bytes(1, 2, 300, 64)) == -4
 
 
 def test_dropout_validation(lib):
