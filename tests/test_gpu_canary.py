@@ -192,7 +192,7 @@ def test_block_sparse_writes_stay_in_bounds():
     assert st == 0
     assert o.intact() and m.intact() and l.intact()
     grads = [Guarded(B * H * N * d * 2) for _ in range(3)]
-    wsb = lib.fa_bwd_workspace_bytes(B, H, N, d)
+    wsb = lib.fa_bwd_block_sparse_workspace_bytes(B, H, N, d)
     ws = Guarded(wsb)
     st = lib.fa_bwd_block_sparse(B, H, N, d, _p(q), _p(k), _p(v), o.ptr,
                                  _p(do), m.ptr, l.ptr, _p(mask), 1, 0.1,
