@@ -1,8 +1,8 @@
 """GPU parity on randomly drawn shapes (a fixed seed, so every run checks the
 same cases): dense forward + backward with causal masks and key padding,
 packed varlen forward + backward, block-sparse and dropout forward +
-backward, paged GQA decode over group sizes 1-16 and 1-64 splits, and paged
-prefill.  Lengths are drawn so that tails are ragged, sequences are empty or
+backward, the FP8 forward (within its derived rounding bound), paged GQA
+decode over group sizes 1-16 and 1-64 splits, and paged prefill.  Lengths are drawn so that tails are ragged, sequences are empty or
 a single token, and some keys collect the dO of many queries.  Each case goes
 through the same checks and tolerances as the dedicated tests.
 
@@ -26,14 +26,15 @@ from tests import test_gpu_decode as tdec
 from tests import test_gpu_fwd as tf
 from tests import test_gpu_prefill as tpre
 from tests import test_gpu_varlen as tv
+from tests import test_gpu_fp8 as t8
 from tests import test_gpu_sparse as tsp
 from tests.helpers import BF16_TOL, assert_close, stored_forward, to_device
 from tests.helpers import to_numpy64
-from workloads import TID_DO, normal, paged_cache
+from workloads import TID_DO, normal, normal_fp8, paged_cache
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ("dense", "varlen", "decode", "prefill", "sparse", "dropout")
+KINDS = ("dense", "varlen", "decode", "prefill", "sparse", "dropout", "fp8")
 PER_KIND = 10
 
 
@@ -77,6 +78,12 @@ def _draw(case):
                           p=float(rng.choice([0.05, 0.1, 0.3, 0.5, 0.8])),
                           dseed=int(rng.integers(0, 1 << 63)),
                           off=int(rng.integers(0, 1 << 20)), seed=seed)
+    if kind == "fp8":
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        N = int(rng.integers(1, 700))
+        kv = ([int(x) for x in rng.integers(1, N + 1, size=B)]
+              if rng.integers(0, 2) else None)
+        return kind, dict(B=B, H=H, N=N, d=d, causal=causal, kv=kv, seed=seed)
     ctx = [int(x) for x in rng.integers(1, 900, size=rng.integers(1, 5))]
     qlen = [int(rng.integers(0, c + 1)) for c in ctx]
     qlen[0] = max(qlen[0], 1)
@@ -205,8 +212,28 @@ def _prefill(ctx, qlen, Hkv, G, d, causal, seed):
     assert np.max(np.abs(l[vis] / rl[vis] - 1)) <= 2.0 ** -8 + 1e-5
 
 
+def _fp8(B, H, N, d, causal, kv, seed):
+    shape = (B, H, N, d)
+    q, qd = normal_fp8(shape, seed, 0)
+    k, kd = normal_fp8(shape, seed, 1)
+    v, vd = normal_fp8(shape, seed, 2, transpose=True)
+    scale = 1 / np.sqrt(d)
+    o, m, l = t8._run(q.store, k.store, v.store, qd, kd, vd, causal, kv,
+                      scale)
+    ro, rm, rl = oracle.attention_fwd(q.exact, k.exact, v.exact, scale, causal,
+                                      kv)
+    A = t8._score_mass(q.exact, k.exact, scale, causal, kv, np.arange(N))
+    t8._check_stats_model(m, l, rm, rl, A)
+    bound, var = t8._fp8_bound(q.exact, k.exact, v.exact, scale, causal, kv,
+                               np.arange(N), rm, rl, ro, A)
+    err = np.abs(o - ro)
+    assert np.all(err <= bound), float(np.max(err / bound))
+    assert np.sqrt(np.mean(err ** 2)) <= np.sqrt(np.mean(var))
+
+
 RUN = {"dense": _dense, "varlen": _varlen, "decode": _decode,
-       "prefill": _prefill, "sparse": _sparse, "dropout": _dropout}
+       "prefill": _prefill, "sparse": _sparse, "dropout": _dropout,
+       "fp8": _fp8}
 
 
 @pytest.mark.parametrize("case", range(PER_KIND * len(KINDS)))
