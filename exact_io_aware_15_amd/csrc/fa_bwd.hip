@@ -589,10 +589,8 @@ __device__ __forceinline__ void bwd_dq_body(const BwdArgs &a, int i) {
   }
 }
 
-// Causal: low key tiles carry most work; dealt so each CU's two resident
-// workgroups (d = 64) carry equal work.
 // The items of each pass in decreasing work, by a counting sort over the
-// work values 0 .. nb (nb <= 8192 for N <= 2^20): workgroup 0 orders the
+// work values 0 .. nb (nb <= 8192: N <= kMaxN = 2^20): workgroup 0 orders the
 // dK/dV items, workgroup 1 the dQ items.  Items of equal work come in any
 // order (each item's result does not depend on when it runs).
 __global__ __launch_bounds__(1024) void sparse_order_kernel(BwdArgs a) {
@@ -647,6 +645,8 @@ __device__ __forceinline__ int sparse_item(const BwdArgs &a, int kind,
   return kind == 0 ? blk * a.BH + bh : (nb - 1 - blk) * a.BH + bh;
 }
 
+// Causal: low key tiles carry most work; dealt so each CU's two resident
+// workgroups (d = 64) carry equal work.  Block-sparse: heaviest items first.
 template <int D, bool CAUSAL, bool PADDED, bool SPARSE = false,
           bool DROP = false>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
