@@ -60,9 +60,8 @@ SMALL = [  # (B, H, N, d, causal, padded)
     (3, 2, 333, 64, True, True),
     (2, 2, 200, 128, False, False),
     (2, 2, 257, 128, True, True),
-    # causal d = 64 runs as mirrored pairs of query tiles with the key tiles
-    # split between two wave groups: one query (one tile, one key), a ragged
-    # second tile, an odd tile count (the middle tile alone), padding
+    # causal d = 64 edge shapes: one query (one tile, one key), a ragged
+    # second query tile, an odd number of query tiles, padding
     (1, 1, 1, 64, True, False),
     (1, 2, 129, 64, True, False),
     (2, 1, 640, 64, True, True),
