@@ -778,7 +778,11 @@ def main():
         kern = "fa_fwd (fwd_bf16_kernel)"
     achieved = cflops / dur / 1e9
     line = {
-        "metric": "attention fwd+bwd TFLOP/s (1 GPU)",
+        # value: TFLOP/s of the fwd+bwd step at the headline shape; the
+        # fraction of the bf16 peak is frac_of_bf16_peak, and the other
+        # lengths from 1K to 16K are in "sweep".
+        "metric": ("attention fwd+bwd TFLOP/s and % of bf16 MFMA peak at "
+                   "N=1K\u201316K (1 GPU)"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
