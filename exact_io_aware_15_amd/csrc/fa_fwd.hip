@@ -265,7 +265,6 @@ __global__ __launch_bounds__(256, MINW) void fwd_bf16_kernel(FwdArgs a) {
   constexpr bool LMF = CAUSAL;
   constexpr int BR = 4 * QPW;                     // queries per workgroup
   constexpr int BC = 64;                          // keys per tile
-  constexpr int CPR = D / 8;                      // 16-byte chunks per row
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BC * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BC * D];
 
