@@ -1,7 +1,9 @@
 """The hot path under HIP graph capture.
 
-fa_fwd + fa_bwd, and the paged decode (with a workspace and without one),
-are captured once and replayed several times.  Between replays the inputs
+Every entry point is captured once and replayed several times: fa_fwd +
+fa_bwd, the paged decode (with a workspace and without one), varlen,
+block-sparse and dropout forward + backward, the FP8 forward and the paged
+prefill.  Between replays the inputs
 are rewritten in place by eager work, with a synchronisation before each
 replay.  Every replay must equal, bit for bit, an eager call on the same
 inputs.  The kernels are deterministic, and the calls allocate nothing,
@@ -108,3 +110,130 @@ def test_decode_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(out, want), f"replay {rep}: decode"
         assert torch.equal(out_na, want), f"replay {rep}: decode (no alloc)"
+
+
+def _replays_match_eager(name, make, step, reps=3):
+    """make(seed) -> list of device tensors; step(*tensors) -> outputs.  The
+    graph is captured on the tensors of make(1); each replay first rewrites
+    them in place with make(seed) for a new seed."""
+    import torch
+    static = make(1)
+    graph, outs = _capture(step, static)
+    for rep in range(reps):
+        print(f"graph {name} replay {rep}", flush=True)
+        fresh = make(700 + rep)
+        for s, f in zip(static, fresh):
+            s.copy_(f)
+        want = [x.clone() for x in step(*fresh)]
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, (got, ref) in enumerate(zip(outs, want)):
+            assert torch.equal(got, ref), f"{name} replay {rep}: output {i}"
+
+
+def test_varlen_graph_replays_match_eager():
+    import numpy as np
+    import torch
+    import exact_io_aware_15_amd as fa
+    lens, H, d = [130, 1, 77, 256], 2, 64
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
+                      device="cuda")
+    total = int(sum(lens))
+
+    def make(seed):
+        return [to_device(normal((H, total, d), seed, t, "bf16"))
+                for t in (0, 1, 2, TID_DO)]
+
+    def step(q, k, v, do):
+        o, m, l = fa.fwd_varlen(q, k, v, cu, max(lens), causal=True)
+        return (o, m, l) + tuple(fa.bwd_varlen(q, k, v, o, do, m, l, cu,
+                                               max(lens), causal=True))
+
+    _replays_match_eager("varlen", make, step)
+
+
+def test_block_sparse_graph_replays_match_eager():
+    import numpy as np
+    import torch
+    import exact_io_aware_15_amd as fa
+    B, H, N, d = 1, 2, 300, 64
+    nb = -(-N // 128)
+    mask = torch.from_numpy(
+        (np.random.default_rng(5).random((H, nb, nb)) < 0.6).astype(
+            np.uint8)).cuda()
+
+    def make(seed):
+        return [to_device(normal((B, H, N, d), seed, t, "bf16"))
+                for t in (0, 1, 2, TID_DO)]
+
+    def step(q, k, v, do):
+        o, m, l = fa.fwd_block_sparse(q, k, v, mask, causal=True)
+        return (o, m, l) + tuple(fa.bwd_block_sparse(q, k, v, o, do, m, l,
+                                                     mask, causal=True))
+
+    _replays_match_eager("block-sparse", make, step)
+
+
+def test_dropout_graph_replays_match_eager():
+    import exact_io_aware_15_amd as fa
+    B, H, N, d = 1, 2, 200, 64
+
+    def make(seed):
+        return [to_device(normal((B, H, N, d), seed, t, "bf16"))
+                for t in (0, 1, 2, TID_DO)]
+
+    def step(q, k, v, do):
+        o, m, l = fa.fwd_dropout(q, k, v, 0.2, 1234, 7, causal=True)
+        return (o, m, l) + tuple(fa.bwd_dropout(q, k, v, o, do, m, l, 0.2,
+                                                1234, 7, causal=True))
+
+    _replays_match_eager("dropout", make, step)
+
+
+def test_fp8_graph_replays_match_eager():
+    import numpy as np
+    import torch
+    import exact_io_aware_15_amd as fa
+    from workloads import normal_fp8
+    shape = (1, 2, 333, 128)
+
+    def dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+    def make(seed):
+        (q, qd), (k, kd), (v, vd) = (normal_fp8(shape, seed, t, transpose=t == 2)
+                                     for t in range(3))
+        return [dev(q.store), dev(k.store), dev(v.store),
+                dev(np.asarray(qd, np.float32)), dev(np.asarray(kd, np.float32)),
+                dev(np.asarray(vd, np.float32))]
+
+    def step(q8, k8, v8, qd, kd, vd):
+        return fa.fwd_fp8(q8, k8, v8, qd, kd, vd, causal=True)
+
+    _replays_match_eager("fp8", make, step)
+
+
+def test_prefill_graph_replays_match_eager():
+    import numpy as np
+    import torch
+    import exact_io_aware_15_amd as fa
+    ctx, new, Hkv, G, d = [300, 40, 129], [64, 1, 129], 2, 2, 128
+    lens = [c + n for c, n in zip(ctx, new)]
+    max_blocks = -(-max(lens) // 16) + 1
+    cache = paged_cache(lens, Hkv, d, 16, max_blocks, 31, poison_tails=True)
+    kc, vc = to_device(cache.k_cache), to_device(cache.v_cache)
+    table = torch.from_numpy(cache.block_table).cuda()
+    seq = torch.from_numpy(cache.seq_lens).cuda()
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(new)]).astype(np.int32),
+                      device="cuda")
+    total = int(sum(new))
+
+    def make(seed):
+        return [to_device(normal((Hkv * G, total, d), seed, 0, "bf16"))]
+
+    def step(q):
+        return fa.prefill_paged(q, kc, vc, table, seq, cu, max(new),
+                                causal=True)
+
+    _replays_match_eager("prefill", make, step)
