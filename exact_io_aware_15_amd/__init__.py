@@ -72,6 +72,19 @@ def _check_dev(name, t, dtype=None, shape=None):
                          f"got {tuple(t.shape)}")
 
 
+def _workspace(workspace, need, device):
+    """The caller's workspace (a contiguous uint8 GPU tensor on the inputs'
+    device; its byte count is passed on, and the library rejects one that is
+    too small) or a new one of the size the library asks for."""
+    torch = _torch()
+    if workspace is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _check_dev("workspace", workspace, torch.uint8)
+    if workspace.device != device:
+        raise ValueError("workspace must be on the inputs' device")
+    return workspace
+
+
 def _stream(t):
     torch = _torch()
     return torch.cuda.current_stream(t.device).cuda_stream
@@ -176,9 +189,8 @@ def bwd(q, k, v, o, do, m, l, causal=False, kv_len=None, scale=None,
     _check_dev("l", l, torch.float32, (B, H, N))
     kv_len = _kv_len(kv_len, B, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    need = bwd_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, bwd_workspace_bytes(B, H, N, d),
+                           q.device)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     with torch.cuda.device(q.device):
         st = lib().fa_bwd(B, H, N, d, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
@@ -232,9 +244,8 @@ def bwd_dropout(q, k, v, o, do, m, l, p_drop, seed, offset=0, causal=False,
     _check_dev("l", l, torch.float32, (B, H, N))
     kv_len = _kv_len(kv_len, B, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    if workspace is None:
-        workspace = torch.empty(bwd_workspace_bytes(B, H, N, d),
-                                dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, bwd_workspace_bytes(B, H, N, d),
+                           q.device)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     with torch.cuda.device(q.device):
         st = lib().fa_bwd_dropout(B, H, N, d, _ptr(q), _ptr(k), _ptr(v),
@@ -292,9 +303,8 @@ def bwd_block_sparse(q, k, v, o, do, m, l, block_mask, causal=False,
     _check_dev("l", l, torch.float32, (B, H, N))
     block_mask = _block_mask(block_mask, H, N, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    if workspace is None:
-        workspace = torch.empty(bwd_block_sparse_workspace_bytes(B, H, N, d),
-                                dtype=torch.uint8, device=q.device)
+    workspace = _workspace(
+        workspace, bwd_block_sparse_workspace_bytes(B, H, N, d), q.device)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     with torch.cuda.device(q.device):
         st = lib().fa_bwd_block_sparse(B, H, N, d, _ptr(q), _ptr(k), _ptr(v),
@@ -359,10 +369,8 @@ def bwd_varlen(q, k, v, o, do, m, l, cu_seqlens, max_seqlen, causal=False,
     _check_dev("l", l, torch.float32, (H, total))
     cu = _cu_seqlens(cu_seqlens, q.device)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    need = bwd_varlen_workspace_bytes(H, total, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8,
-                                device=q.device)
+    workspace = _workspace(workspace, bwd_varlen_workspace_bytes(H, total, d),
+                           q.device)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     with torch.cuda.device(q.device):
         st = lib().fa_bwd_varlen(cu.numel() - 1, H, total, int(max_seqlen), d,
@@ -462,10 +470,9 @@ def decode_paged(q, k_cache, v_cache, block_table, seq_lens, num_splits=8,
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [B, max_blocks]")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    need = decode_workspace_bytes(B, Hq, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8,
-                                device=q.device)
+    workspace = _workspace(workspace,
+                           decode_workspace_bytes(B, Hq, d, num_splits),
+                           q.device)
     out = torch.empty_like(q)
     with torch.cuda.device(q.device):
         st = lib().fa_decode_paged(B, Hq, Hkv, d, _ptr(q), _ptr(k_cache),
