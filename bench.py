@@ -722,8 +722,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the attention kernels shard over independent (batch, head) "
-              "units, and a multi-GPU run is not part of this build.",
+              "the attention kernels would shard over independent "
+              "(batch, head) units, but multi-GPU runs are not supported.",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -230,7 +230,7 @@ const char *fa_status_str(int status) {
     case FA_OK: return "FA_OK";
     case FA_E_NULLPTR: return "FA_E_NULLPTR: a required pointer is NULL";
     case FA_E_SHAPE: return "FA_E_SHAPE: size out of range or inconsistent";
-    case FA_E_UNSUPPORTED: return "FA_E_UNSUPPORTED: not implemented in this build";
+    case FA_E_UNSUPPORTED: return "FA_E_UNSUPPORTED: not implemented by the library";
     case FA_E_WORKSPACE: return "FA_E_WORKSPACE: workspace missing or too small";
     case FA_E_HIP: return "FA_E_HIP: HIP runtime error at launch";
     case FA_E_SCRATCH:

@@ -44,7 +44,7 @@ typedef enum {
   FA_OK = 0,
   FA_E_NULLPTR = -1,     /* a required pointer is NULL                         */
   FA_E_SHAPE = -2,       /* a size is out of range or inconsistent             */
-  FA_E_UNSUPPORTED = -3, /* valid request this build does not implement        */
+  FA_E_UNSUPPORTED = -3, /* a valid request the library does not implement     */
   FA_E_WORKSPACE = -4,   /* workspace missing or smaller than the query says   */
   FA_E_HIP = -5,         /* the HIP runtime reported an error at launch        */
   FA_E_SCRATCH = -6      /* request larger than the library's fixed scratch    */
